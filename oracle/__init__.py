@@ -1,0 +1,25 @@
+"""fp64 CPU oracle for training-free Dual Chunk Attention (DCA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product library imports, calls or
+links anything in this package; only the tests, the smoke check and the CPU
+baseline leg of the benchmark use it.  It shares no code with the HIP path.
+"""
+from .dca_ref import (  # noqa: F401
+    chunk_size,
+    rope_inv_freq,
+    rope_rotate,
+    key_position,
+    query_positions,
+    relation,
+    relative_position_table,
+    remap_positions,
+    rope_remap_ref,
+    dca_prefill_ref,
+    dca_prefill_formB,
+    dca_decode_ref,
+    MAP_KEY,
+    MAP_Q_INTRA,
+    MAP_Q_SUCC,
+    MAP_Q_INTER,
+    MAP_PLAIN,
+)
