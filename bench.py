@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the DCA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * DCA causal prefill of the Llama2-70B-shaped 32k workload (B 1, 64 query /
+    8 KV heads, D 128, L 32768, c 4096, w 1024) = prepare (cos/sin table, key
+    rotation, V transpose) + the fused attention kernel, and
+  * DCA decode of 16 sequences against a 100001-token cache (64/8 heads, D 128).
+Inputs are generated once (seeded, synthetic) and are resident in HBM before
+the timed region.  Timing uses HIP events recorded on the stream the library
+launches on (torch's current stream).
+
+Printed JSON (one line, stdout):
+  value        prefill TFLOP/s at 32k = algorithmic FLOPs / (prepare + attend)
+  ms_per_step  wall time of one step (prefill + decode), timed region / K
+  roofline     the attention kernel against the bf16 dense MFMA peak
+  decode       decode GB/s against the HBM peak
+  prefill_128k the same prefill at 131072 tokens
+  cpu_baseline the fp64 oracle timed on a bounded sample of rows on the host
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DCA prefill TFLOP/s (% bf16 MFMA peak) at 32k/128k; decode GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attend_llama2_70b_32k_traffic.json")
+KERNEL_SOURCES = ["long_context_attention_dca_amd/csrc/prefill.hip",
+                  "long_context_attention_dca_amd/csrc/dca_common.hpp"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, L, Hq, D):
+    """One QK^T and one PV multiply-add per causal pair (diagonal included)."""
+    return 4.0 * B * Hq * D * L * (L + 1) / 2.0
+
+
+def decode_bytes(B, kv_len, Hq, Hkv, D, esize=2):
+    """K and V caches read once, plus q in and o out."""
+    return B * kv_len * Hkv * D * esize * 2 + 2 * B * Hq * D * esize
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, cfg, seconds):
+    """The oracle as it stands, on seeded random rows of one head, for ~`seconds`."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    L, D = cfg["L"], cfg["D"]
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, L, size=4096)
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while done < len(rows):
+        batch = rows[done:done + 32]
+        oracle.dca_prefill_ref(q, k, v, cfg["c"], cfg["w"], cfg["base"], rows=batch, heads=[0])
+        flops += sum(4.0 * D * (int(i) + 1) for i in batch)
+        done += len(batch)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{done} seeded random query rows of head 0 of the llama2_70b_32k prefill "
+                      f"(fp64 NumPy form A), {dt:.1f} s; host cores available "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-128k", action="store_true", help="skip the 131072-token prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k"], default=None,
+                    help="run one workload only (for profiling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_attention_dca_amd as dca
+    from long_context_attention_dca_amd import inputs
+
+    if not os.path.exists(dca.library_path()):
+        from long_context_attention_dca_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    P = inputs.WORKLOADS["llama2_70b_32k"]
+    DC = inputs.WORKLOADS["decode_100k"]
+    P128 = inputs.WORKLOADS["llama2_70b_128k"]
+    run_prefill = args.only in (None, "prefill")
+    run_decode = args.only in (None, "decode")
+    run_128k = (args.only == "prefill128k") or (args.only is None and not args.no_128k)
+
+    # ---------------- inputs, resident in HBM before timing ----------------
+    if run_prefill:
+        log("generating llama2_70b_32k inputs")
+        q_h, k_h, v_h = inputs.prefill_inputs(P["B"], P["L"], P["Hq"], P["Hkv"], P["D"], "bf16", P["seed"])
+        q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
+        o = torch.empty_like(q)
+        nbytes = dca.prefill_workspace_bytes(P["B"], P["L"], P["Hkv"], P["D"], P["c"], torch.bfloat16)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if run_decode:
+        log("generating decode_100k inputs")
+        dq_h, dk_h, dv_h = inputs.decode_inputs(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"], "bf16",
+                                                DC["seed"])
+        dq = dq_h.to(dev)
+        kraw = dk_h.to(dev)
+        del dk_h
+        kc = dca.rope_remap(kraw, dca.DCA_MAP_KEY, DC["c"], DC["w"], DC["base"], 0)
+        del kraw
+        vc = dv_h.to(dev)
+        del dv_h
+        dws = torch.empty(dca.decode_workspace_bytes(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"],
+                                                     torch.bfloat16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill_step(q_, k_, v_, o_, ws_, cfg, ev):
+        ev[0].record()
+        dca.prefill_prepare(k_, v_, cfg["c"], cfg["w"], cfg["base"], workspace=ws_)
+        ev[1].record()
+        dca.prefill_attend(q_, ws_, cfg["Hkv"], cfg["c"], cfg["w"], out=o_)
+        ev[2].record()
+
+    def decode_step(ev):
+        ev[0].record()
+        out = dca.decode(dq, kc, vc, DC["c"], DC["w"], DC["base"], workspace=dws)
+        ev[1].record()
+        return out
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # ---------------- the step: prefill 32k + decode 100k ----------------
+    pe = [events(3) for _ in range(args.steps)]
+    de = [events(2) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        if run_prefill:
+            prefill_step(q, k, v, o, ws, P, events(3))
+        if run_decode:
+            decode_step(events(2))
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if run_prefill:
+            prefill_step(q, k, v, o, ws, P, pe[i])
+        if run_decode:
+            decode_step(de[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if run_prefill:
+        prep_ms = sum(e[0].elapsed_time(e[1]) for e in pe) / args.steps
+        att_ms = sum(e[1].elapsed_time(e[2]) for e in pe) / args.steps
+        fl = prefill_flops(P["B"], P["L"], P["Hq"], P["D"])
+        result["value"] = fl / ((prep_ms + att_ms) * 1e-3) / 1e12
+        result["unit"] = "TFLOP/s"
+        achieved = fl / (att_ms * 1e-3) / 1e12
+        traffic = measured_traffic()
+        result["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                              "traffic": traffic, "kernel": "prefill_bf16_kernel<128>",
+                              "kernel_ms": att_ms, "flops_per_launch": fl}
+        result["prefill_32k"] = {"ms": prep_ms + att_ms, "prepare_ms": prep_ms, "attend_ms": att_ms,
+                                 "tflops": result["value"]}
+    if run_decode:
+        dec_ms = sum(e[0].elapsed_time(e[1]) for e in de) / args.steps
+        nb = decode_bytes(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"])
+        gbps = nb / (dec_ms * 1e-3) / 1e9
+        result["decode"] = {"ms": dec_ms, "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": gbps / PEAK_HBM_GBPS, "bytes_per_call": nb, "bound": "hbm"}
+        if not run_prefill:
+            result["value"], result["unit"] = gbps, "GB/s"
+    cfg = {"workload": "llama2_70b_32k prefill + decode_100k" if run_prefill and run_decode else
+           ("llama2_70b_32k prefill" if run_prefill else "decode_100k"),
+           "prefill": {k_: P[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")},
+           "decode": {k_: DC[k_] for k_ in ("B", "kv_len", "Hq", "Hkv", "D", "c", "w")}}
+    result["config"] = cfg
+
+    # ---------------- 128k prefill (reported beside the step) ----------------
+    if run_128k:
+        if run_prefill:
+            del o, ws
+        if run_decode:
+            del kc, vc, dws
+        torch.cuda.empty_cache()
+        log("generating llama2_70b_128k inputs")
+        q2h, k2h, v2h = inputs.prefill_inputs(P128["B"], P128["L"], P128["Hq"], P128["Hkv"], P128["D"], "bf16",
+                                              P128["seed"])
+        q2, k2, v2 = q2h.to(dev), k2h.to(dev), v2h.to(dev)
+        del q2h, k2h, v2h
+        o2 = torch.empty_like(q2)
+        ws2 = torch.empty(dca.prefill_workspace_bytes(P128["B"], P128["L"], P128["Hkv"], P128["D"], P128["c"],
+                                                      torch.bfloat16), dtype=torch.uint8, device=dev)
+        n128 = max(1, min(args.steps, 3))
+        prefill_step(q2, k2, v2, o2, ws2, P128, events(3))
+        torch.cuda.synchronize()
+        ev128 = [events(3) for _ in range(n128)]
+        for i in range(n128):
+            prefill_step(q2, k2, v2, o2, ws2, P128, ev128[i])
+        torch.cuda.synchronize()
+        prep = sum(e[0].elapsed_time(e[1]) for e in ev128) / n128
+        att = sum(e[1].elapsed_time(e[2]) for e in ev128) / n128
+        fl = prefill_flops(P128["B"], P128["L"], P128["Hq"], P128["D"])
+        result["prefill_128k"] = {"ms": prep + att, "prepare_ms": prep, "attend_ms": att,
+                                  "tflops": fl / ((prep + att) * 1e-3) / 1e12,
+                                  "attend_tflops": fl / (att * 1e-3) / 1e12,
+                                  "frac": fl / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "steps": n128}
+        if args.only == "prefill128k":
+            result["value"], result["unit"] = result["prefill_128k"]["tflops"], "TFLOP/s"
+            result["config"] = {"workload": "llama2_70b_128k prefill",
+                                "prefill": {k_: P128[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
+
+    if run_prefill and not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(q_h, k_h, v_h, P, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * dca.h - C ABI of the MI355X (gfx950) Dual Chunk Attention library.
+ *
+ * Dual Chunk Attention (DCA) is the training-free long-context method of
+ * "Training-Free Long-Context Scaling of Large Language Models" (abstract),
+ * described operationally in "Dual-Chunk Attention: Training-Free 100k+
+ * Context Guide" (sections "The Architecture", "Intra-Chunk Attention",
+ * "Inter-Chunk Attention", "Successive Chunk Smoothing" and "Flash-DCA").
+ *
+ * Parameters of every call: pretrain length c, local window w, chunk size
+ * s = c - w, RoPE base.  Positions used (0 <= w < c):
+ *   key j                          : P_k = j mod s
+ *   query i, same chunk (intra)    : P_q = i mod s
+ *   query i, previous chunk (succ) : P_q = min(s + (i mod s), c - 1)
+ *   query i, older chunks (inter)  : P_q = c - 1
+ * The chunk relation of a pair is floor(i/s) - floor(j/s) (0, 1, >= 2).
+ * RoPE uses the rotate-half pairing (k, k + D/2) with
+ * theta_k = base^(-2k/D); attention is causal with the diagonal included.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  Scratch memory comes from the
+ *     caller through (ws, ws_bytes); size it with the *_workspace_bytes query.
+ *   - Layouts are dense and contiguous: Q/K/V/O are [B, L, H, D] ("BSHD"),
+ *     LSE is [B, Hq, L] fp32.  Tensor pointers must be 16-byte aligned and the
+ *     workspace 256-byte aligned.
+ *   - dtype: DCA_F32 or DCA_BF16, the type of Q/K/V/O (and of caches).  LSE and
+ *     all accumulation are fp32.  Head dim D must be 64 or 128.
+ *   - GQA: Hq must be a multiple of Hkv; query head h reads KV head
+ *     floor(h * Hkv / Hq) (contiguous groups).
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous: a return of DCA_OK means "enqueued".  Device faults surface
+ *     at the caller's next synchronisation.
+ *   - Argument validation happens before any HIP call, so an invalid call
+ *     returns its error without touching the device.  No C++ exception
+ *     crosses this interface.  Calls on different streams with distinct
+ *     workspaces are independent; the library keeps no global state.
+ */
+#ifndef DCA_H_
+#define DCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+#define DCA_F32 0
+#define DCA_BF16 1
+
+/* Position maps of dca_rope_remap (see the position table above). */
+#define DCA_MAP_KEY 0     /* P = t mod s                      */
+#define DCA_MAP_Q_INTRA 1 /* P = t mod s                      */
+#define DCA_MAP_Q_SUCC 2  /* P = min(s + (t mod s), c - 1)    */
+#define DCA_MAP_Q_INTER 3 /* P = c - 1                        */
+#define DCA_MAP_PLAIN 4   /* P = t (ordinary RoPE)            */
+
+/* Status codes. */
+#define DCA_OK 0
+#define DCA_ERR_INVALID_ARG (-1) /* null pointer, bad shape, w >= c, Hq % Hkv != 0, misalignment */
+#define DCA_ERR_UNSUPPORTED (-2) /* head dim or dtype the kernels do not implement               */
+#define DCA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the query returned          */
+#define DCA_ERR_HIP (-4)         /* a HIP launch reported an error                                */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* dca_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int dca_version(void);
+
+/*
+ * dca_rope_remap - rotate every head vector of x by its DCA position.
+ *
+ * Definition: the RoPE rotation of "Dual-Chunk Attention: Training-Free 100k+
+ * Context Guide", section "The Problem" (angle = position * theta_k per
+ * rotary pair), applied at the chunk-local positions of the sections
+ * "Intra-Chunk Attention" / "Inter-Chunk Attention" / "Successive Chunk
+ * Smoothing" as listed in the header comment.  Token t (0 <= t < L) of x is
+ * at absolute position pos0 + t; `map` picks which DCA position it is rotated
+ * to.  DCA_MAP_KEY is how a decode KV cache is built; the query maps expose
+ * the three query variants the attention kernels form internally.
+ *
+ *   x, out : [B, L, H, D] of `dtype`, device; out may equal x (in place).
+ *   pos0   : >= 0, position of token 0.
+ *   map    : one of DCA_MAP_*.
+ * Angles, cos/sin and the rotation are evaluated in fp64; the result is
+ * rounded to nearest even into the output type (bf16 through fp32).
+ */
+int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
+                   int64_t pos0, int map, int c, int w, double rope_base, int dtype,
+                   void* stream);
+
+/*
+ * Scratch bytes dca_prefill needs for these sizes (0 on invalid sizes).
+ * Holds the fp64 rope cos/sin table [c, D/2], the rotated keys (head-major,
+ * padded to a multiple of 64 rows) and the values (bf16: tiled transpose;
+ * fp32: a copy).
+ */
+size_t dca_prefill_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c,
+                                   int dtype);
+
+/*
+ * dca_prefill - DCA causal attention over a whole sequence (prefill).
+ *
+ * Definition: for every query i and key j <= i, the score is
+ *   sm_scale * < R_{P_q(i, rho)} q_i , R_{P_k(j)} k_j >
+ * with the query variant chosen by the pair's chunk relation rho ("The
+ * Architecture" taxonomy box and the three region sections of the DCA
+ * guide); scores are merged with a flash-style online softmax over key tiles
+ * ("Flash-DCA: Fusing DCA into FlashAttention Tiling Loops"), so the L x L
+ * matrix is never stored.
+ *
+ *   q         : [B, L, Hq, D] raw (pre-RoPE) queries.
+ *   k, v      : [B, L, Hkv, D] raw keys, values.
+ *   o         : [B, L, Hq, D] output.
+ *   lse       : [B, Hq, L] fp32 natural-log log-sum-exp of the scaled scores,
+ *               or NULL.
+ *   k_rot_out : [B, L, Hkv, D] keys rotated at j mod s (a decode KV cache), or
+ *               NULL.
+ *   sm_scale  : softmax scale; <= 0 selects 1/sqrt(D).
+ *   ws        : scratch of at least dca_prefill_workspace_bytes(...) bytes.
+ * bf16 runs QK^T and PV on bf16 MFMA with fp32 accumulation (rotated q/k and
+ * the probabilities are rounded to bf16 before each product); fp32 runs in
+ * fp32 throughout.
+ */
+int dca_prefill(const void* q, const void* k, const void* v, void* o, float* lse, void* k_rot_out,
+                int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
+                double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+                void* stream);
+
+/*
+ * The two phases dca_prefill runs, exposed so a caller can prepare K/V once
+ * and time or repeat the attention phase on its own.
+ *
+ * dca_prefill_prepare: builds, inside ws, the fp64 cos/sin table for positions
+ * [0, c), the keys rotated at j mod s (head-major, rows padded to a multiple
+ * of 64) and the value layout the attention kernel reads (bf16: a tiled
+ * transpose; fp32: a copy).  k_rot_out as in dca_prefill (may be NULL).
+ *
+ * dca_prefill_attend: the fused attention kernel over a workspace prepared by
+ * dca_prefill_prepare with the same B, L, Hkv, D, c, w, rope_base and dtype
+ * (not checked: a mismatch gives wrong results, not an error).  q, o, lse as
+ * in dca_prefill.
+ */
+int dca_prefill_prepare(const void* k, const void* v, void* k_rot_out, int64_t B, int64_t L,
+                        int64_t Hkv, int64_t D, int c, int w, double rope_base, int dtype,
+                        void* ws, size_t ws_bytes, void* stream);
+int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L, int64_t Hq,
+                       int64_t Hkv, int64_t D, int c, int w, float sm_scale, int dtype,
+                       const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Scratch bytes dca_decode needs for these sizes (0 on invalid sizes): the
+ * three rotated query variants and the per-split partial results.
+ */
+size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
+                                  int dtype);
+
+/*
+ * dca_decode - one new query token per sequence against a long KV cache.
+ *
+ * Definition: row q_pos = kv_len - 1 of dca_prefill (the cache holds the new
+ * token itself), computed split-K: the cache is cut into key ranges processed
+ * in parallel and merged by log-sum-exp ("Strategic Recommendations": pair
+ * DCA with FlashDecoding, which splits the KV cache across the GPU).
+ *
+ *   q        : [B, Hq, D] raw query of the new token.
+ *   k_cache  : [B, kv_len, Hkv, D] keys ALREADY rotated at j mod s (from
+ *              dca_rope_remap(DCA_MAP_KEY, pos0 = 0) or dca_prefill's k_rot_out).
+ *   v_cache  : [B, kv_len, Hkv, D] values.
+ *   o        : [B, Hq, D] output; lse : [B, Hq] fp32 or NULL.
+ *   ws       : scratch of at least dca_decode_workspace_bytes(...) bytes.
+ */
+int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+               int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
+               double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCA_H_ */

@@ -1,0 +1,188 @@
+"""MI355X (gfx950) Dual Chunk Attention: thin Python binding of the C ABI.
+
+Every step of the computation runs in the HIP kernels of ``libdca_mi355x.so``;
+this module only checks tensors, allocates outputs/workspaces through PyTorch
+(device memory and the current stream are all PyTorch supplies) and passes
+pointers.  There is no CPU fallback: if the library is missing, every entry
+point raises.
+
+Entry points (same names as include/dca.h):
+  rope_remap(x, map, c, w, base=1e4, pos0=0, out=None)
+  prefill(q, k, v, c, w, base=1e4, sm_scale=None, return_lse=False,
+          return_k_rot=False, workspace=None)
+  decode(q, k_cache, v_cache, c, w, base=1e4, sm_scale=None,
+         return_lse=False, workspace=None)
+  prefill_workspace_bytes(...), decode_workspace_bytes(...)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    DCA_BF16, DCA_F32, DCA_MAP_KEY, DCA_MAP_PLAIN, DCA_MAP_Q_INTER, DCA_MAP_Q_INTRA,
+    DCA_MAP_Q_SUCC, DCAError,
+)
+
+__all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
+           "prefill_workspace_bytes", "decode_workspace_bytes", "DCAError", "library_path"]
+
+_DT = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"dtype {t.dtype} not supported (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _check(t: torch.Tensor, name: str, ndim: int, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def prefill_workspace_bytes(B, L, Hkv, D, c, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(_lib.load().dca_prefill_workspace_bytes(B, L, Hkv, D, c, code))
+
+
+def decode_workspace_bytes(B, kv_len, Hq, Hkv, D, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(_lib.load().dca_decode_workspace_bytes(B, kv_len, Hq, Hkv, D, code))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a GPU buffer of at least {nbytes} bytes")
+    return workspace
+
+
+def rope_remap(x: torch.Tensor, map: int, c: int, w: int, base: float = 10000.0, pos0: int = 0,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rotate x [B, L, H, D] by the DCA position map `map` (token t at pos0 + t)."""
+    lib = _lib.load()
+    _check(x, "x", 4)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", 4, x.dtype)
+    B, L, H, D = x.shape
+    _lib.check("dca_rope_remap", lib.dca_rope_remap(
+        x.data_ptr(), out.data_ptr(), B, L, H, D, pos0, map, c, w, float(base), _dtype_code(x),
+        _stream(x.device)))
+    return out
+
+
+def prefill(q, k, v, c: int, w: int, base: float = 10000.0, sm_scale: float | None = None,
+            return_lse: bool = False, return_k_rot: bool = False, workspace=None):
+    """DCA causal prefill.  q [B, L, Hq, D], k/v [B, L, Hkv, D] raw; returns o (and lse, k_rot)."""
+    lib = _lib.load()
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, L, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    code = _dtype_code(q)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, L, dtype=torch.float32, device=q.device) if return_lse else None
+    k_rot = torch.empty_like(k) if return_k_rot else None
+    nbytes = int(lib.dca_prefill_workspace_bytes(B, L, Hkv, D, c, code))
+    if nbytes == 0:
+        raise ValueError("invalid prefill sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_prefill", lib.dca_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), _ptr(k_rot),
+        B, L, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    res = [o]
+    if return_lse:
+        res.append(lse)
+    if return_k_rot:
+        res.append(k_rot)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def prefill_prepare(k, v, c: int, w: int, base: float = 10000.0, workspace=None,
+                    k_rot_out: torch.Tensor | None = None) -> torch.Tensor:
+    """Phase 1 of prefill: build the rotated-key / value workspace; returns it."""
+    lib = _lib.load()
+    _check(k, "k", 4)
+    _check(v, "v", 4, k.dtype)
+    B, L, Hkv, D = k.shape
+    code = _dtype_code(k)
+    nbytes = int(lib.dca_prefill_workspace_bytes(B, L, Hkv, D, c, code))
+    if nbytes == 0:
+        raise ValueError("invalid prefill sizes")
+    ws = _workspace(nbytes, k.device, workspace)
+    if k_rot_out is not None:
+        _check(k_rot_out, "k_rot_out", 4, k.dtype)
+    _lib.check("dca_prefill_prepare", lib.dca_prefill_prepare(
+        k.data_ptr(), v.data_ptr(), _ptr(k_rot_out), B, L, Hkv, D, c, w, float(base), code,
+        ws.data_ptr(), nbytes, _stream(k.device)))
+    return ws
+
+
+def prefill_attend(q, workspace, Hkv: int, c: int, w: int, sm_scale: float | None = None,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Phase 2 of prefill: the attention kernel over a prepared workspace."""
+    lib = _lib.load()
+    _check(q, "q", 4)
+    B, L, Hq, D = q.shape
+    code = _dtype_code(q)
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", 4, q.dtype)
+    nbytes = int(lib.dca_prefill_workspace_bytes(B, L, Hkv, D, c, code))
+    _lib.check("dca_prefill_attend", lib.dca_prefill_attend(
+        q.data_ptr(), o.data_ptr(), _ptr(lse), B, L, Hq, Hkv, D, c, w, float(sm_scale or 0.0), code,
+        workspace.data_ptr(), min(nbytes, workspace.numel() * workspace.element_size()),
+        _stream(q.device)))
+    return o
+
+
+def decode(q, k_cache, v_cache, c: int, w: int, base: float = 10000.0, sm_scale: float | None = None,
+           return_lse: bool = False, workspace=None):
+    """DCA decode of one token per sequence: q [B, Hq, D] raw; caches [B, kv_len, Hkv, D],
+    keys already rotated at j mod s.  The token sits at position kv_len - 1."""
+    lib = _lib.load()
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4, q.dtype)
+    _check(v_cache, "v_cache", 4, q.dtype)
+    B, Hq, D = q.shape
+    kv_len, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, kv_len, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    code = _dtype_code(q)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(lib.dca_decode_workspace_bytes(B, kv_len, Hq, Hkv, D, code))
+    if nbytes == 0:
+        raise ValueError("invalid decode sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_decode", lib.dca_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), _ptr(lse),
+        B, kv_len, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o

@@ -1,0 +1,257 @@
+// abi.hip - the extern "C" entry points declared in include/dca.h.
+//
+// Every argument is validated on the host before the first HIP call, so an
+// invalid call returns its status without touching the device.  Scratch space
+// is carved from the caller's workspace; the library allocates nothing and
+// keeps no state between calls.
+#include <math.h>
+#include <stdint.h>
+
+#include "dca.h"
+#include "dca_launch.hpp"
+
+using namespace dca;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // per-dimension bound (grid sizes, int indices)
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool dtype_ok(int dtype) { return dtype == DCA_F32 || dtype == DCA_BF16; }
+bool head_dim_ok(int64_t D) { return D == 64 || D == 128; }
+int64_t elem_size(int dtype) { return dtype == DCA_F32 ? 4 : 2; }
+bool cw_ok(int c, int w) { return c >= 1 && c <= (1 << 24) && w >= 0 && w < c; }
+bool base_ok(double base) { return base > 0.0 && isfinite(base); }
+
+struct PrefillLayout {
+  int64_t Lp;
+  size_t table, krot, vt, total;
+};
+
+bool prefill_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c, int dtype,
+                    PrefillLayout* out) {
+  if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype) || c < 1) return false;
+  if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
+  PrefillLayout p;
+  p.Lp = round_up(L, kPrefillTileKeys);
+  const int64_t tbytes = (int64_t)c * (D / 2) * 16;
+  const int64_t kbytes = B * Hkv * p.Lp * D * elem_size(dtype);
+  const int64_t vbytes = B * Hkv * p.Lp * D * elem_size(dtype);
+  p.table = 0;
+  p.krot = (size_t)round_up(tbytes, 256);
+  p.vt = p.krot + (size_t)round_up(kbytes, 256);
+  p.total = p.vt + (size_t)round_up(vbytes, 256);
+  *out = p;
+  return true;
+}
+
+struct DecodeLayout {
+  int kps, ns;
+  size_t qv, part_o, part_lse, total;
+};
+
+bool decode_layout(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D, int dtype,
+                   DecodeLayout* out) {
+  if (B < 1 || kv_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D) || !dtype_ok(dtype))
+    return false;
+  if (B >= kMaxDim || kv_len >= kMaxDim / 2 || Hq >= 65536 || B * Hq >= kMaxDim) return false;
+  DecodeLayout p;
+  decode_plan(B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
+  p.qv = 0;
+  p.part_o = (size_t)round_up(B * Hq * 3 * D * elem_size(dtype), 256);
+  p.part_lse = p.part_o + (size_t)round_up(B * Hq * (int64_t)p.ns * D * 4, 256);
+  p.total = p.part_lse + (size_t)round_up(B * Hq * (int64_t)p.ns * 4, 256);
+  *out = p;
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DCA_OK : DCA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dca_status_string(int status) {
+  switch (status) {
+    case DCA_OK:
+      return "DCA_OK: success (work enqueued)";
+    case DCA_ERR_INVALID_ARG:
+      return "DCA_ERR_INVALID_ARG: null pointer, bad shape, w >= c, Hq % Hkv != 0 or misaligned pointer";
+    case DCA_ERR_UNSUPPORTED:
+      return "DCA_ERR_UNSUPPORTED: head dim must be 64 or 128 and dtype DCA_F32 or DCA_BF16";
+    case DCA_ERR_WORKSPACE:
+      return "DCA_ERR_WORKSPACE: workspace missing, misaligned or smaller than the size query";
+    case DCA_ERR_HIP:
+      return "DCA_ERR_HIP: a HIP launch reported an error";
+    default:
+      return "unknown DCA status";
+  }
+}
+
+int dca_version(void) { return 10000; }
+
+int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D, int64_t pos0,
+                   int map, int c, int w, double rope_base, int dtype, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!x || !out || B < 0 || L < 0 || H < 0 || pos0 < 0) return DCA_ERR_INVALID_ARG;
+  if (B >= kMaxDim || L >= kMaxDim || H >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
+  if (!cw_ok(c, w) || map < DCA_MAP_KEY || map > DCA_MAP_PLAIN || !base_ok(rope_base))
+    return DCA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16)) return DCA_ERR_INVALID_ARG;
+  if (B == 0 || L == 0 || H == 0) return DCA_OK;
+  return hip_status(launch_rope_remap(x, out, B, L, H, D, pos0, map, c, w, rope_base, dtype,
+                                      (hipStream_t)stream));
+}
+
+size_t dca_prefill_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c, int dtype) {
+  PrefillLayout p;
+  return prefill_layout(B, L, Hkv, D, c, dtype, &p) ? p.total : 0;
+}
+
+static int prefill_common_checks(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c, int w,
+                                 int dtype, const void* ws, size_t ws_bytes, PrefillLayout* p) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (B < 1 || L < 1 || Hkv < 1 || !cw_ok(c, w)) return DCA_ERR_INVALID_ARG;
+  if (!prefill_layout(B, L, Hkv, D, c, dtype, p)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p->total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+  return DCA_OK;
+}
+
+static int prepare_impl(const void* k, const void* v, void* k_rot_out, int64_t B, int64_t L,
+                        int64_t Hkv, int64_t D, int c, int w, double rope_base, int dtype,
+                        void* ws, const PrefillLayout& p, hipStream_t st) {
+  uint8_t* base = (uint8_t*)ws;
+  double2* table = (double2*)(base + p.table);
+  hipError_t e = launch_rope_table(table, c, (int)D, rope_base, st);
+  if (e != hipSuccess) return DCA_ERR_HIP;
+  e = launch_kv_prep(k, v, table, base + p.krot, base + p.vt, k_rot_out, B, L, p.Lp, Hkv, D, c - w,
+                     dtype, st);
+  if (e != hipSuccess) return DCA_ERR_HIP;
+  if (dtype == DCA_F32) {
+    e = hipMemcpyAsync(base + p.vt, v, (size_t)(B * L * Hkv * D * 4), hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return DCA_ERR_HIP;
+  }
+  return DCA_OK;
+}
+
+static int attend_impl(const void* q, void* o, float* lse, int64_t B, int64_t L, int64_t Hq,
+                       int64_t Hkv, int64_t D, int c, int w, float sm_scale, int dtype,
+                       const void* ws, const PrefillLayout& p, hipStream_t st) {
+  const uint8_t* base = (const uint8_t*)ws;
+  PrefillArgs a;
+  a.q = q;
+  a.krot = base + p.krot;
+  a.vt = base + p.vt;
+  a.table = (const double2*)(base + p.table);
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.L = (int)L;
+  a.Lp = (int)p.Lp;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.D = (int)D;
+  a.c = c;
+  a.w = w;
+  a.s = c - w;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+  return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
+}
+
+static bool attend_args_ok(const void* q, const void* o, const float* lse, int64_t B, int64_t L,
+                           int64_t Hq, int64_t Hkv, float sm_scale) {
+  if (!q || !o || Hq < 1 || Hkv < 1 || Hq % Hkv || Hq >= 65536) return false;
+  if (B * Hq * ((L + 127) / 128) >= kMaxDim || !isfinite(sm_scale)) return false;
+  return aligned(q, 16) && aligned(o, 16) && (!lse || aligned(lse, 4));
+}
+
+int dca_prefill_prepare(const void* k, const void* v, void* k_rot_out, int64_t B, int64_t L,
+                        int64_t Hkv, int64_t D, int c, int w, double rope_base, int dtype,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16) || (k_rot_out && !aligned(k_rot_out, 16)) ||
+      !base_ok(rope_base))
+    return DCA_ERR_INVALID_ARG;
+  PrefillLayout p;
+  const int r = prefill_common_checks(B, L, Hkv, D, c, w, dtype, ws, ws_bytes, &p);
+  if (r != DCA_OK) return r;
+  return prepare_impl(k, v, k_rot_out, B, L, Hkv, D, c, w, rope_base, dtype, ws, p,
+                      (hipStream_t)stream);
+}
+
+int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L, int64_t Hq,
+                       int64_t Hkv, int64_t D, int c, int w, float sm_scale, int dtype,
+                       const void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!attend_args_ok(q, o, lse, B, L, Hq, Hkv, sm_scale)) return DCA_ERR_INVALID_ARG;
+  PrefillLayout p;
+  const int r = prefill_common_checks(B, L, Hkv, D, c, w, dtype, ws, ws_bytes, &p);
+  if (r != DCA_OK) return r;
+  return attend_impl(q, o, lse, B, L, Hq, Hkv, D, c, w, sm_scale, dtype, ws, p,
+                     (hipStream_t)stream);
+}
+
+int dca_prefill(const void* q, const void* k, const void* v, void* o, float* lse, void* k_rot_out,
+                int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
+                double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16) || (k_rot_out && !aligned(k_rot_out, 16)) ||
+      !base_ok(rope_base) || !attend_args_ok(q, o, lse, B, L, Hq, Hkv, sm_scale))
+    return DCA_ERR_INVALID_ARG;
+  PrefillLayout p;
+  const int r = prefill_common_checks(B, L, Hkv, D, c, w, dtype, ws, ws_bytes, &p);
+  if (r != DCA_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  const int rp = prepare_impl(k, v, k_rot_out, B, L, Hkv, D, c, w, rope_base, dtype, ws, p, st);
+  if (rp != DCA_OK) return rp;
+  return attend_impl(q, o, lse, B, L, Hq, Hkv, D, c, w, sm_scale, dtype, ws, p, st);
+}
+
+size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
+                                  int dtype) {
+  DecodeLayout p;
+  return decode_layout(B, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+}
+
+int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+               int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
+               double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !o) return DCA_ERR_INVALID_ARG;
+  if (B < 1 || kv_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return DCA_ERR_INVALID_ARG;
+  if (!cw_ok(c, w) || !base_ok(rope_base) || !isfinite(sm_scale)) return DCA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return DCA_ERR_INVALID_ARG;
+  DecodeLayout p;
+  if (!decode_layout(B, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+
+  uint8_t* base = (uint8_t*)ws;
+  DecodeArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.qv = base + p.qv;
+  a.part_o = (float*)(base + p.part_o);
+  a.part_lse = (float*)(base + p.part_lse);
+  a.B = (int)B;
+  a.kv_len = (int)kv_len;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.D = (int)D;
+  a.c = c;
+  a.w = w;
+  a.s = c - w;
+  a.base = rope_base;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+  a.keys_per_split = p.kps;
+  a.nsplit = p.ns;
+  return hip_status(launch_decode(a, dtype, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,380 @@
+// decode.hip - DCA decode: one new query token per sequence against a long KV cache.
+//
+// The new token sits at position q_pos = kv_len - 1, so the result is row
+// q_pos of the DCA prefill definition ("Dual-Chunk Attention: Training-Free
+// 100k+ Context Guide", sections "The Architecture" .. "Successive Chunk
+// Smoothing").  Work is split over the cache ("Strategic Recommendations":
+// pair DCA with FlashDecoding, which splits the KV cache across the GPU's
+// compute units) and merged by log-sum-exp.
+//
+// Three launches:
+//   1. qprep   : the three rotated variants of every query head (fp64 angles).
+//   2. split   : each wave streams one contiguous key range of one (batch,
+//                KV head) and keeps an online softmax for the GQA group's query
+//                heads (up to 32 per pass, the N side of a 32x32 MFMA).  K and
+//                V rows are read with fully coalesced 16-byte loads; K goes to
+//                LDS as swizzled rows, V is transposed into LDS while being
+//                stored (16-bit stores), so both MFMA products read 16-byte
+//                fragments.  Partials (normalised O and log2-domain LSE) go to
+//                the workspace.
+//   3. combine : log-sum-exp merge of the partials per query head.
+#include "dca_common.hpp"
+#include "dca_launch.hpp"
+
+namespace dca {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleThreshold = 8.0f;
+constexpr float kNoMax = -1.0e30f;  // running-max sentinel (finite)
+constexpr int SUB = 32;  // keys per wave sub-tile
+
+__device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ inline int vt_perm(int p) { return (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+template <int NCK>
+__device__ inline int swz(int row, int chunk) {
+  if constexpr (NCK == 16)
+    return chunk ^ (row & 15);
+  else if constexpr (NCK == 8)
+    return chunk ^ ((row >> 1) & 7);
+  else
+    return chunk ^ ((row >> 2) & 3);
+}
+
+// ---- 1. query variants -------------------------------------------------------------
+template <typename T>
+__global__ void decode_qprep_kernel(const T* __restrict__ q, T* __restrict__ qv, int D, int c, int s,
+                                    int qpos, double base) {
+  const int bh = blockIdx.x, k = threadIdx.x;
+  const int half = D / 2;
+  if (k >= half) return;
+  const T* src = q + (int64_t)bh * D;
+  const double x1 = Elem<T>::load(src + k), x2 = Elem<T>::load(src + k + half);
+  const double theta = pow(base, -2.0 * (double)k / (double)D);
+  const int r = qpos % s;
+#pragma unroll
+  for (int cls = 0; cls < 3; ++cls) {
+    double sn, cs;
+    sincos((double)query_pos(cls, r, s, c) * theta, &sn, &cs);
+    T* dst = qv + ((int64_t)bh * 3 + cls) * D;
+    Elem<T>::store(dst + k, (float)(x1 * cs - x2 * sn));
+    Elem<T>::store(dst + k + half, (float)(x2 * cs + x1 * sn));
+  }
+}
+
+// ---- 2. split kernel, bf16 MFMA ----------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int CPR = D / 8;             // 16-byte chunks per cache row
+  constexpr int NI = SUB * CPR / 64;     // load instructions per sub-tile per tensor
+  constexpr int KBYTES = SUB * D * 2;
+  constexpr int WBYTES = 2 * KBYTES;     // K rows + V^T, per wave
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * WBYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5, ql = lane & 31;
+  const int split = blockIdx.x * 4 + wave;
+  if (split >= a.nsplit) return;
+  const int unit = blockIdx.y;  // (b, g, query group)
+  const int qg = unit % nqg;
+  const int bg = unit / nqg;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int qi = qg * 32 + ql;   // index inside the GQA group
+  const bool qvalid = qi < G;
+  const int hq = g * G + (qvalid ? qi : 0);
+  const int kv_len = a.kv_len, s = a.s;
+  const int kbeg = split * a.keys_per_split;
+  const int kend = min(kbeg + a.keys_per_split, kv_len);
+  const int qpos = kv_len - 1;
+  const int nq = qpos / s;
+
+  uint8_t* kl = smem + wave * WBYTES;
+  uint8_t* vl = kl + KBYTES;
+  const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive keys
+  const uint16_t* kc = (const uint16_t*)a.kc + ((int64_t)b * kv_len * a.Hkv + g) * D;
+  const uint16_t* vc = (const uint16_t*)a.vc + ((int64_t)b * kv_len * a.Hkv + g) * D;
+  const uint16_t* qv = (const uint16_t*)a.qv + ((int64_t)b * a.Hq + hq) * 3 * D;
+
+  bf16x8 qf[NDS];
+  auto load_q = [&](int cls) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const uint4 u = qvalid ? *(const uint4*)(qv + cls * D + ds * 16 + hh * 8) : make_uint4(0, 0, 0, 0);
+      qf[ds] = as_bf16x8(u);
+    }
+  };
+
+  uint4 kreg[NI], vreg[NI];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int id = it * 64 + lane;
+      const int row = id / CPR, ch = id % CPR;
+      const int j = j0 + row;
+      if (j < kend) {
+        kreg[it] = *(const uint4*)(kc + (int64_t)j * row_stride + ch * 8);
+        vreg[it] = *(const uint4*)(vc + (int64_t)j * row_stride + ch * 8);
+      } else {
+        kreg[it] = make_uint4(0, 0, 0, 0);
+        vreg[it] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int id = it * 64 + lane;
+      const int row = id / CPR, ch = id % CPR;
+      *(uint4*)(kl + row * (D * 2) + swz<CPR>(row, ch) * 16) = kreg[it];
+      const int p = vt_perm(row);
+      const uint32_t w[4] = {vreg[it].x, vreg[it].y, vreg[it].z, vreg[it].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = ch * 8 + e;
+        const uint16_t val = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+        *(uint16_t*)(vl + d * 64 + swz<4>(d, p >> 3) * 16 + (p & 7) * 2) = val;
+      }
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+  float m_run = kNoMax, l_run = 0.f;
+  int cur_cls = -1;
+
+  gload(kbeg);
+  for (int j0 = kbeg; j0 < kend; j0 += SUB) {
+    __builtin_amdgcn_wave_barrier();
+    lstore();
+    __builtin_amdgcn_wave_barrier();
+    if (j0 + SUB < kend) gload(j0 + SUB);
+
+    const int jl = min(j0 + SUB, kend) - 1;
+    const int cls_lo = min(nq - jl / s, 2), cls_hi = min(nq - j0 / s, 2);
+    const bool straddle = cls_lo != cls_hi;
+    const bool tail = j0 + SUB > kend;
+    // A sub-tile spanning several relations is processed once per relation
+    // with the other pairs masked; the online softmax merges the pieces.
+    for (int cls = cls_lo; cls <= cls_hi; ++cls) {
+      if (cls != cur_cls) {
+        load_q(cls);
+        cur_cls = cls;
+      }
+      // Keep the fragment reads inside this (rarely repeated) loop.
+      int toff = wave * WBYTES;
+      asm volatile("" : "+v"(toff));
+      const uint8_t* kl = smem + toff;
+      const uint8_t* vl = kl + KBYTES;
+      f32x16 sacc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int ch = ds * 2 + hh;
+        const bf16x8 kf = *(const bf16x8*)(kl + ql * (D * 2) + swz<CPR>(ql, ch) * 16);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc, 0, 0, 0);
+      }
+      if (tail || straddle) {
+        // Keys kept: the split's range, intersected on a straddling sub-tile
+        // with the key range of relation `cls` (intra: chunk nq, successive:
+        // chunk nq-1, inter: chunks < nq-1).
+        int lo = kbeg, hi = kend - 1;
+        if (straddle) {
+          lo = max(lo, cls == 0 ? nq * s : (cls == 1 ? (nq - 1) * s : 0));
+          hi = min(hi, cls == 0 ? qpos : (cls == 1 ? nq * s - 1 : (nq - 1) * s - 1));
+        }
+        const int jb = j0 + hh * 4;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = jb + (v >> 2) * 8 + (v & 3);
+          sacc[v] = (j >= lo && j <= hi) ? sacc[v] : -INFINITY;
+        }
+      }
+      float mx = sacc[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = mx * scale_log2;
+      if (__any(mnew > m_run + kRescaleThreshold)) {
+        const float mn = fmaxf(m_run, mnew);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        m_run = mn;
+      }
+      float lsum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u * 8 + e], scale_log2, -m_run));
+          lsum += p[e];
+        }
+        const bf16x8 pf = as_bf16x8(pack_bf16x8(p));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int d = db * 32 + ql;
+          const bf16x8 vf = *(const bf16x8*)(vl + d * 64 + swz<4>(d, u * 2 + hh) * 16);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+        }
+      }
+      l_run += lsum;
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qvalid) {
+    const int64_t pidx = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
+    float* po = a.part_o + pidx * D;
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        float4 o4 = make_float4(oacc[db][grp * 4] * inv, oacc[db][grp * 4 + 1] * inv,
+                                oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv);
+        *(float4*)(po + db * 32 + grp * 8 + hh * 4) = o4;
+      }
+    if (hh == 0) a.part_lse[pidx] = m_run + log2f(l_tot);
+  }
+}
+
+// ---- 2'. split kernel, fp32 (VALU) -------------------------------------------------
+// One workgroup per (batch, query head, split); 256 keys scored per step.
+__global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
+  __shared__ float qs[3][128];
+  __shared__ float sc[256];
+  __shared__ float red[8];
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int D = a.D;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const int G = a.Hq / a.Hkv, g = hq / G;
+  const int kv_len = a.kv_len, s = a.s;
+  const int kbeg = split * a.keys_per_split;
+  const int kend = min(kbeg + a.keys_per_split, kv_len);
+  const int nq = (kv_len - 1) / s;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const float* qv = (const float*)a.qv + (int64_t)bh * 3 * D;
+  for (int idx = tid; idx < 3 * D; idx += 256) qs[idx / D][idx % D] = qv[idx];
+  const int64_t row_stride = (int64_t)a.Hkv * D;
+  const float* kc = (const float*)a.kc + ((int64_t)b * kv_len * a.Hkv + g) * D;
+  const float* vc = (const float*)a.vc + ((int64_t)b * kv_len * a.Hkv + g) * D;
+  float m = -INFINITY, l = 0.f, o = 0.f;  // thread tid < D owns output dim tid
+  __syncthreads();
+  for (int jb = kbeg; jb < kend; jb += 256) {
+    const int j = jb + tid;
+    float x = -INFINITY;
+    if (j < kend) {
+      const int cls = min(nq - j / s, 2);
+      const float* kr = kc + (int64_t)j * row_stride;
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qs[cls][d], kr[d], acc);
+      x = acc * a.sm_scale;
+    }
+    float mx = x;
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) red[wid] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float mn = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float p = (x == -INFINITY) ? 0.f : expf(x - mn);
+    sc[tid] = p;
+    float ps = p;
+    for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    __syncthreads();
+    if (lane == 0) red[4 + wid] = ps;
+    __syncthreads();
+    l = l * alpha + (red[4] + red[5] + red[6] + red[7]);
+    m = mn;
+    if (tid < D) {
+      float acc = o * alpha;
+      const int nk = min(256, kend - jb);
+      for (int t = 0; t < nk; ++t) acc = fmaf(sc[t], vc[(int64_t)(jb + t) * row_stride + tid], acc);
+      o = acc;
+    }
+    __syncthreads();
+  }
+  if (tid < D) {
+    const int64_t pidx = (int64_t)bh * a.nsplit + split;
+    a.part_o[pidx * D + tid] = o / l;
+    if (tid == 0) a.part_lse[pidx] = (m + logf(l)) * kLog2e;
+  }
+}
+
+// ---- 3. combine ----------------------------------------------------------------------
+template <typename T>
+__global__ void decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                      T* __restrict__ o, float* __restrict__ lse, int D, int ns) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* pl = part_lse + (int64_t)bh * ns;
+  float M = -INFINITY;
+  for (int i = 0; i < ns; ++i) M = fmaxf(M, pl[i]);
+  float wsum = 0.f, acc = 0.f;
+  const float* po = part_o + (int64_t)bh * ns * D;
+  for (int i = 0; i < ns; ++i) {
+    const float wgt = exp2f(pl[i] - M);
+    wsum += wgt;
+    if (d < D) acc = fmaf(wgt, po[(int64_t)i * D + d], acc);
+  }
+  if (d < D) Elem<T>::store(o + (int64_t)bh * D + d, acc / wsum);
+  if (d == 0 && lse) lse[bh] = (M + log2f(wsum)) * kLn2;
+}
+
+}  // namespace
+
+void decode_plan(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int dtype, int* keys_per_split,
+                 int* nsplit) {
+  const int64_t G = Hq / Hkv;
+  const int64_t units = dtype == 0 ? B * Hq : B * Hkv * ((G + 31) / 32);
+  const int64_t target = dtype == 0 ? 2048 : 8192;  // concurrent workers to aim for
+  int64_t per = (target + units - 1) / units;
+  if (per < 1) per = 1;
+  int64_t kps = (kv_len + per - 1) / per;
+  kps = round_up(kps < 256 ? 256 : kps, SUB);
+  *keys_per_split = (int)kps;
+  *nsplit = (int)((kv_len + kps - 1) / kps);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
+  const int qpos = a.kv_len - 1;
+  const int nbh = a.B * a.Hq;
+  if (dtype == 0) {
+    hipLaunchKernelGGL(decode_qprep_kernel<float>, dim3(nbh), dim3(64), 0, st, (const float*)a.q,
+                       (float*)a.qv, a.D, a.c, a.s, qpos, a.base);
+    hipLaunchKernelGGL(decode_split_f32_kernel, dim3(a.nsplit, nbh), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(nbh), dim3(128), 0, st, a.part_o, a.part_lse,
+                       (float*)a.o, a.lse, a.D, a.nsplit);
+  } else {
+    hipLaunchKernelGGL(decode_qprep_kernel<uint16_t>, dim3(nbh), dim3(64), 0, st,
+                       (const uint16_t*)a.q, (uint16_t*)a.qv, a.D, a.c, a.s, qpos, a.base);
+    const int G = a.Hq / a.Hkv;
+    const int nqg = (G + 31) / 32;
+    const dim3 grid((unsigned)((a.nsplit + 3) / 4), (unsigned)(a.B * a.Hkv * nqg));
+    const float scale_log2 = a.sm_scale * kLog2e;
+    if (a.D == 64)
+      hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, dim3(256), 0, st, a, nqg, scale_log2);
+    else
+      hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, dim3(256), 0, st, a, nqg, scale_log2);
+    hipLaunchKernelGGL(decode_combine_kernel<uint16_t>, dim3(nbh), dim3(128), 0, st, a.part_o,
+                       a.part_lse, (uint16_t*)a.o, a.lse, a.D, a.nsplit);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dca

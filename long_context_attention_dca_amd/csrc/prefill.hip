@@ -1,0 +1,446 @@
+// prefill.hip - DCA causal prefill attention kernels for gfx950.
+//
+// What is computed ("Dual-Chunk Attention: Training-Free 100k+ Context
+// Guide", sections "The Architecture", "Intra-Chunk Attention", "Inter-Chunk
+// Attention", "Successive Chunk Smoothing" and "Flash-DCA"): for query i and
+// key j <= i the score is sm_scale * <R_{P_q} q_i, R_{j mod s} k_j>, where P_q
+// is one of three query positions picked by the chunk relation of (i, j).  The
+// softmax over j is merged tile by tile (online max / sum), so no L x L matrix
+// exists.  When the chunk size is a multiple of the tile sizes every (query
+// tile, key tile) pair has one relation, and a tile costs exactly what a plain
+// flash-attention tile costs; otherwise a straddling tile is processed once
+// per relation it contains, with the other relations' pairs masked out.
+//
+// bf16 kernel layout (one workgroup = 4 waves = 128 query rows of one head):
+//   * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
+//     wave's 32 rotated queries held in registers.  In the 32x32 output layout
+//     each lane owns one query column, so the row max / sum need a single
+//     cross-half exchange.
+//   * O^T += V^T * P^T on the same MFMA: A = V^T rows from LDS (pre-transposed
+//     and key-permuted by the prep pass), B = the probabilities straight from
+//     the S^T registers.
+//   * K and V^T tiles of 64 keys are double-buffered in LDS, filled by direct
+//     global->LDS loads (no staging registers) in XOR-swizzled 16-byte chunks
+//     so the MFMA fragment reads are conflict free; one barrier per tile.
+//   * The query variant lives in registers and is re-made (rotate raw Q with the
+//     cos/sin table) only when the tile relation changes: inter -> successive
+//     -> intra, at most three times per workgroup on the fast path.
+//   * Online softmax in the log2 domain; rescaling of the accumulator is skipped
+//     while the running max grows by less than 8 (exact: O and l share the
+//     stale max).
+//   * Workgroups are ordered longest causal row first, and, when B*Hkv is a
+//     multiple of 8, mapped so that each XCD (workgroup id mod 8) serves whole
+//     GQA groups and their K/V stay in that XCD's L2.
+#include "dca_common.hpp"
+#include "dca_launch.hpp"
+
+namespace dca {
+
+namespace {
+
+constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int BC = kPrefillTileKeys;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleThreshold = 8.0f;
+constexpr float kNoMax = -1.0e30f;  // running-max sentinel (finite)
+
+// 16-byte chunk swizzle for LDS tiles whose rows are NCK chunks long.
+template <int NCK>
+__device__ inline int swz(int row, int chunk) {
+  if constexpr (NCK == 16)
+    return chunk ^ (row & 15);
+  else
+    return chunk ^ ((row >> 1) & 7);
+}
+
+template <int D>
+struct Smem {
+  static constexpr int KBYTES = BC * D * 2;
+  static constexpr int VBYTES = D * BC * 2;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int TOTAL = 2 * STAGE;
+};
+
+__device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// s_waitcnt vmcnt(0): this wave's global loads (including the direct-to-LDS
+// ones) have landed.  Encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
+  constexpr int NDS = D / 16;          // MFMA k-steps over the head dim
+  constexpr int NDB = D / 32;          // 32-row blocks of O^T
+  constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  constexpr int KLD = BC * KCH / 256;  // K chunks staged per thread per tile
+  constexpr int VLD = D * 8 / 256;     // V^T chunks staged per thread per tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<D>::TOTAL];
+
+  // ---- work item ------------------------------------------------------------
+  const int wg = blockIdx.x;
+  int qt_rank, b, hq;
+  const int G = a.Hq / a.Hkv;
+  if (xcd_map) {
+    const int xcd = wg & 7, k = wg >> 3;
+    const int per_rank = (a.B * a.Hkv / 8) * G;
+    qt_rank = k / per_rank;
+    const int rem = k - qt_rank * per_rank;
+    const int slot = (rem / G) * 8 + xcd;
+    b = slot / a.Hkv;
+    hq = (slot - b * a.Hkv) * G + rem % G;
+  } else {
+    const int bh = a.B * a.Hq;
+    qt_rank = wg / bh;
+    const int rem = wg - qt_rank * bh;
+    b = rem / a.Hq;
+    hq = rem - b * a.Hq;
+  }
+  const int qt = nqt - 1 - qt_rank;
+  const int g = hq / G;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5, ql = lane & 31;
+  const int L = a.L, s = a.s, c = a.c;
+  const int i0 = qt * BR;
+  const int qrow = i0 + wave * 32 + ql;
+  const int i_lo = i0 + wave * 32;
+  const int i_hi = min(i_lo + 31, L - 1);
+  const bool wave_live = i_lo < L;
+  const int n_lo = i_lo / s, n_hi = wave_live ? i_hi / s : 0;
+  const int nq = qrow / s, rq = qrow - nq * s;
+  const int last_key = min(i0 + BR - 1, L - 1);
+  const int nkt = last_key / BC + 1;
+
+  const uint16_t* qsrc = (const uint16_t*)a.q + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+  const uint16_t* kbase = (const uint16_t*)a.krot + bg * (int64_t)a.Lp * D;
+  const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
+
+  // ---- query variant in registers (B operand of S^T = K Q^T) ------------------
+  // Lane (query ql, half hh) holds dims d = ds*16 + hh*8 + e; the rotate-half
+  // partner d + D/2 is in step ds + NDS/2 of the same lane.
+  bf16x8 qf[NDS];
+  auto load_q = [&](int cls) {
+    const int P = query_pos(cls, rq, s, c);
+    const double2* tb = a.table + (int64_t)P * (D / 2);
+    if (qrow < L) {
+#pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds) {
+        const uint4 u1 = *(const uint4*)(qsrc + ds * 16 + hh * 8);
+        const uint4 u2 = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
+        float x1[8], x2[8], y1[8], y2[8];
+        unpack_bf16x8(u1, x1);
+        unpack_bf16x8(u2, x2);
+        // Rotation in fp64, one rounding to bf16 (through fp32).
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double2 t = tb[ds * 16 + hh * 8 + e];
+          y1[e] = (float)((double)x1[e] * t.x - (double)x2[e] * t.y);
+          y2[e] = (float)((double)x2[e] * t.x + (double)x1[e] * t.y);
+        }
+        qf[ds] = as_bf16x8(pack_bf16x8(y1));
+        qf[ds + NDS / 2] = as_bf16x8(pack_bf16x8(y2));
+      }
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) qf[ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  };
+
+  // ---- K / V^T staging: direct global -> LDS loads ----------------------------
+  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS base + 16*l, so the
+  // swizzle is applied on the global side: the lane that lands on physical
+  // chunk p of a row fetches logical chunk swz(row, p) (the swizzle is an XOR,
+  // hence its own inverse).  Each wave issues a quarter of the 1-KB pieces.
+  constexpr int KPW = BC * D * 2 / 1024 / 4;  // K pieces per wave per tile
+  constexpr int VPW = D * BC * 2 / 1024 / 4;  // V^T pieces per wave per tile
+  auto issue_tile = [&](int kt, int stage) {
+    const uint16_t* ks = kbase + (int64_t)kt * BC * D;
+    const uint16_t* vs = vbase + (int64_t)kt * BC * D;
+    uint8_t* kb = smem + stage * Smem<D>::STAGE;
+    uint8_t* vb = kb + Smem<D>::KBYTES;
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int r = wave * KPW + i;
+      const int byte = r * 1024 + lane * 16;
+      const int row = byte / (D * 2), pch = (byte % (D * 2)) / 16;
+      __builtin_amdgcn_global_load_lds((const void*)(ks + row * D + swz<KCH>(row, pch) * 8),
+                                       (__attribute__((address_space(3))) void*)(kb + r * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const int r = wave * VPW + i;
+      const int byte = r * 1024 + lane * 16;
+      const int row = byte >> 7, pch = (byte & 127) >> 4;
+      __builtin_amdgcn_global_load_lds((const void*)(vs + row * BC + swz<8>(row, pch) * 8),
+                                       (__attribute__((address_space(3))) void*)(vb + r * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+  // Running max (log2 domain).  The finite sentinel keeps rows that have seen
+  // no unmasked key yet NaN-free: their p is exp2(-inf) = 0 and alpha is 1.
+  float m_run = kNoMax, l_run = 0.f;
+  int cur_cls = -1;
+
+  issue_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nkt) issue_tile(kt + 1, stage ^ 1);
+    const int j0 = kt * BC;
+    if (wave_live && j0 <= i_hi) {
+      // Chunk relations present among the unmasked pairs of this wave x tile.
+      const int jmax = min(j0 + BC - 1, i_hi);
+      const int rho_lo = max(n_lo - jmax / s, 0);
+      const int rho_hi = n_hi - j0 / s;
+      const int cls_lo = min(rho_lo, 2), cls_hi = min(rho_hi, 2);
+      const bool straddle = cls_lo != cls_hi;
+      const bool causal = j0 + BC - 1 > i_lo;
+      // A tile whose pairs fall in several relations is processed once per
+      // relation, with the other relations' pairs masked out; the online
+      // softmax merges the pieces like ordinary tiles.
+      for (int cls = cls_lo; cls <= cls_hi; ++cls) {
+        if (cls != cur_cls) {
+          load_q(cls);
+          cur_cls = cls;
+        }
+        // The tile's LDS offset goes through an empty asm so the fragment
+        // reads below are not hoisted out of this (rarely repeated) loop.
+        int toff = stage * Smem<D>::STAGE;
+        asm volatile("" : "+v"(toff));
+        const uint8_t* kb = smem + toff;
+        const uint8_t* vb = kb + Smem<D>::KBYTES;
+        f32x16 sacc[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int row = kb2 * 32 + ql, ch = ds * 2 + hh;
+            const bf16x8 kf = *(const bf16x8*)(kb + row * (D * 2) + swz<KCH>(row, ch) * 16);
+            sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb2], 0, 0, 0);
+          }
+        }
+        if (causal || straddle) {
+          // Keys this lane keeps: the causal prefix j <= qrow, intersected on a
+          // straddling tile with the key range of relation `cls` for this row
+          // (intra: chunk nq, successive: chunk nq-1, inter: chunks < nq-1).
+          int lo = 0, hi = qrow;
+          if (straddle) {
+            lo = cls == 0 ? nq * s : (cls == 1 ? (nq - 1) * s : 0);
+            hi = min(hi, cls == 0 ? qrow : (cls == 1 ? nq * s - 1 : (nq - 1) * s - 1));
+          }
+          const int jb = j0 + hh * 4;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int j = jb + kb2 * 32 + (v >> 2) * 8 + (v & 3);
+              sacc[kb2][v] = (j >= lo && j <= hi) ? sacc[kb2][v] : -INFINITY;
+            }
+        }
+
+        // ---- online softmax (log2 domain) ----
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb2][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = mx * scale_log2;
+        if (__any(mnew > m_run + kRescaleThreshold)) {
+          const float mn = fmaxf(m_run, mnew);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+          m_run = mn;
+        }
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][u * 8 + e], scale_log2, -m_run));
+              lsum += p[e];
+            }
+            const bf16x8 pf = as_bf16x8(pack_bf16x8(p));
+            // ---- O^T += V^T P^T for this 16-key group ----
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const int row = db * 32 + ql, ch = (kb2 * 2 + u) * 2 + hh;
+              const bf16x8 vf = *(const bf16x8*)(vb + row * 128 + swz<8>(row, ch) * 16);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+            }
+          }
+        }
+        l_run += lsum;
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue ----------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow < L) {
+    const float inv = 1.f / l_tot;
+    uint16_t* dst = (uint16_t*)a.o + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        uint2 wv;
+        wv.x = pack_bf16x2(oacc[db][grp * 4] * inv, oacc[db][grp * 4 + 1] * inv);
+        wv.y = pack_bf16x2(oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv);
+        *(uint2*)(dst + db * 32 + grp * 8 + hh * 4) = wv;
+      }
+    if (hh == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---- fp32 kernel (VALU, exact-arithmetic path for fp32 inputs) ---------------------
+// One workgroup = 16 query rows of one head; 16 lanes per row, 32-key tiles.
+constexpr int FBR = 16, FBC = 32;
+
+template <int D>
+__global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
+  constexpr int HALF = D / 2;
+  constexpr int NO = D / 16;
+  __shared__ float qv[3][D][FBR];
+  __shared__ float ks[FBC][D + 1];
+  __shared__ float vs[FBC][D];
+  __shared__ float ps[FBR][FBC + 1];
+  const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int L = a.L, s = a.s, c = a.c;
+  const int G = a.Hq / a.Hkv, g = hq / G;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int tid = threadIdx.x;
+  const int r = tid >> 4, kq = tid & 15;
+  const int i0 = qt * FBR, i = i0 + r;
+  const float* q = (const float*)a.q;
+  const float* krot = (const float*)a.krot + bg * (int64_t)a.Lp * D;
+  const float* vraw = (const float*)a.vt;
+
+  for (int idx = tid; idx < FBR * HALF; idx += 256) {
+    const int rr = idx / HALF, k = idx - rr * HALF;
+    const int ii = i0 + rr;
+    float x1 = 0.f, x2 = 0.f;
+    if (ii < L) {
+      const float* src = q + (((int64_t)b * L + ii) * a.Hq + hq) * D;
+      x1 = src[k];
+      x2 = src[k + HALF];
+    }
+    const int rqq = ii % s;
+#pragma unroll
+    for (int cls = 0; cls < 3; ++cls) {
+      const double2 t = a.table[(int64_t)query_pos(cls, rqq, s, c) * HALF + k];
+      qv[cls][k][rr] = (float)((double)x1 * t.x - (double)x2 * t.y);
+      qv[cls][k + HALF][rr] = (float)((double)x2 * t.x + (double)x1 * t.y);
+    }
+  }
+  float m = -INFINITY, l = 0.f, o[NO];
+#pragma unroll
+  for (int u = 0; u < NO; ++u) o[u] = 0.f;
+  const int nq = i / s;
+  const int last_key = min(i0 + FBR - 1, L - 1);
+  const int nkt = last_key / FBC + 1;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int j0 = kt * FBC;
+    __syncthreads();
+    for (int idx = tid; idx < FBC * D; idx += 256) {
+      const int row = idx / D, d = idx - row * D;
+      const int j = j0 + row;
+      ks[row][d] = krot[(int64_t)j * D + d];
+      vs[row][d] = (j < L) ? vraw[(((int64_t)b * L + j) * a.Hkv + g) * D + d] : 0.f;
+    }
+    __syncthreads();
+    float sc[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = kq * 2 + e, j = j0 + key;
+      if (j > i || j >= L) {
+        sc[e] = -INFINITY;
+      } else {
+        const int cls = min(nq - j / s, 2);
+        float acc = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], ks[key][d], acc);
+        sc[e] = acc * a.sm_scale;
+      }
+    }
+    float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mn = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float p0 = (sc[0] == -INFINITY) ? 0.f : expf(sc[0] - mn);
+    const float p1 = (sc[1] == -INFINITY) ? 0.f : expf(sc[1] - mn);
+    float psum = p0 + p1;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
+    l = l * alpha + psum;
+    m = mn;
+    ps[r][kq * 2] = p0;
+    ps[r][kq * 2 + 1] = p1;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int d = kq + 16 * u;
+      float acc = o[u] * alpha;
+#pragma unroll 8
+      for (int key = 0; key < FBC; ++key) acc = fmaf(ps[r][key], vs[key][d], acc);
+      o[u] = acc;
+    }
+  }
+  if (i < L) {
+    float* dst = (float*)a.o + (((int64_t)b * L + i) * a.Hq + hq) * D;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int u = 0; u < NO; ++u) dst[kq + 16 * u] = o[u] * inv;
+    if (kq == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + i] = m + logf(l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
+  const int nqt = (a.L + BR - 1) / BR;
+  const int64_t total = (int64_t)nqt * a.B * a.Hq;
+  const int xcd_map = ((int64_t)a.B * a.Hkv) % 8 == 0 ? 1 : 0;
+  const float scale_log2 = a.sm_scale * kLog2e;
+  if (a.D == 64)
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)total), dim3(256), 0, st, a, nqt,
+                       xcd_map, scale_log2);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)total), dim3(256), 0, st, a, nqt,
+                       xcd_map, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.L + FBR - 1) / FBR), (unsigned)a.Hq, (unsigned)a.B);
+  if (a.D == 64)
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dca

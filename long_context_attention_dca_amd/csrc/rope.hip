@@ -1,0 +1,179 @@
+// rope.hip - RoPE table, the dca_rope_remap kernel and the prefill K/V prep pass.
+//
+// RoPE ("Dual-Chunk Attention: Training-Free 100k+ Context Guide", section
+// "The Problem"): the pair (x_k, x_{k+D/2}) is turned by position * theta_k,
+// theta_k = base^(-2k/D).  DCA positions ("The Architecture" box and the
+// intra / inter / successive sections): keys at j mod s, queries at one of
+// three positions chosen by the chunk relation.
+#include "dca_common.hpp"
+#include "dca_launch.hpp"
+
+namespace dca {
+
+// ---- cos/sin table [c][D/2] (fp64) -------------------------------------------------
+__global__ void rope_table_kernel(double2* __restrict__ table, int c, int half, int D, double base) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= c * half) return;
+  const int p = idx / half, k = idx - p * half;
+  const double theta = pow(base, -2.0 * (double)k / (double)D);
+  double sn, cs;
+  sincos((double)p * theta, &sn, &cs);
+  table[idx] = make_double2(cs, sn);
+}
+
+hipError_t launch_rope_table(double2* table, int c, int D, double base, hipStream_t st) {
+  const int half = D / 2;
+  const int n = c * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, c, half, D,
+                     base);
+  return hipGetLastError();
+}
+
+// ---- dca_rope_remap -----------------------------------------------------------------
+// One workgroup per token t: the 64 (or 32) angles of its position are made
+// once in fp64 and applied to every (batch, head) row of that token.
+__device__ inline int64_t remap_position(int64_t p, int map, int c, int w) {
+  const int64_t s = c - w;
+  switch (map) {
+    case 0:  // key
+    case 1:  // query, intra
+      return p % s;
+    case 2: {  // query, successive
+      const int64_t r = p % s;
+      return (s + r < c) ? s + r : (int64_t)(c - 1);
+    }
+    case 3:  // query, inter
+      return c - 1;
+    default:  // plain RoPE
+      return p;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) rope_remap_kernel(const T* __restrict__ x, T* __restrict__ out,
+                                                         int64_t B, int64_t L, int H, int D,
+                                                         int64_t pos0, int map, int c, int w,
+                                                         double base) {
+  __shared__ double2 cs[64];
+  const int64_t t = blockIdx.x;
+  const int half = D / 2;
+  const int64_t P = remap_position(pos0 + t, map, c, w);
+  if ((int)threadIdx.x < half) {
+    const double theta = pow(base, -2.0 * (double)threadIdx.x / (double)D);
+    double sn, cn;
+    sincos((double)P * theta, &sn, &cn);
+    cs[threadIdx.x] = make_double2(cn, sn);
+  }
+  __syncthreads();
+  const int64_t per_b = (int64_t)H * half;
+  for (int64_t idx = threadIdx.x; idx < B * per_b; idx += blockDim.x) {
+    const int64_t b = idx / per_b;
+    const int rem = (int)(idx - b * per_b);
+    const int h = rem / half, k = rem - h * half;
+    const int64_t off = ((b * L + t) * H + h) * D;
+    const double x1 = Elem<T>::load(x + off + k);
+    const double x2 = Elem<T>::load(x + off + k + half);
+    const double2 a = cs[k];
+    Elem<T>::store(out + off + k, (float)(x1 * a.x - x2 * a.y));
+    Elem<T>::store(out + off + k + half, (float)(x2 * a.x + x1 * a.y));
+  }
+}
+
+hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
+                             int64_t pos0, int map, int c, int w, double base, int dtype,
+                             hipStream_t st) {
+  if (L == 0 || B == 0 || H == 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(rope_remap_kernel<float>, dim3((unsigned)L), dim3(256), 0, st,
+                       (const float*)x, (float*)out, B, L, (int)H, (int)D, pos0, map, c, w, base);
+  else
+    hipLaunchKernelGGL(rope_remap_kernel<uint16_t>, dim3((unsigned)L), dim3(256), 0, st,
+                       (const uint16_t*)x, (uint16_t*)out, B, L, (int)H, (int)D, pos0, map, c, w,
+                       base);
+  return hipGetLastError();
+}
+
+// ---- prefill K/V prep ---------------------------------------------------------------
+// Within each 16-key group of a V^T tile the keys are stored in the order
+// 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the key index swapped).  That is the
+// order in which one half-wave holds the probabilities of a 16-key step in the
+// 32x32 MFMA output layout, so the PV step reads 8 contiguous keys per lane.
+__device__ inline int vt_perm(int p) { return (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+template <typename T, int D, bool TRANSPOSE_V>
+__global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                      const double2* __restrict__ table,
+                                                      T* __restrict__ krot, uint16_t* __restrict__ vt,
+                                                      T* __restrict__ k_rot_out, int L, int Lp, int Hkv,
+                                                      int s) {
+  constexpr int half = D / 2;
+  constexpr int TK = kPrefillTileKeys;
+  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int j0 = tile * TK;
+  const int64_t bg = (int64_t)b * Hkv + g;
+  for (int idx = threadIdx.x; idx < TK * half; idx += 256) {
+    const int row = idx / half, kk = idx - row * half;
+    const int j = j0 + row;
+    T* dst = krot + (bg * Lp + j) * D;
+    if (j < L) {
+      const int64_t in = (((int64_t)b * L + j) * Hkv + g) * D;
+      const double x1 = Elem<T>::load(k + in + kk);
+      const double x2 = Elem<T>::load(k + in + kk + half);
+      const double2 a = table[(j % s) * half + kk];
+      const float y1 = (float)(x1 * a.x - x2 * a.y);
+      const float y2 = (float)(x2 * a.x + x1 * a.y);
+      Elem<T>::store(dst + kk, y1);
+      Elem<T>::store(dst + kk + half, y2);
+      if (k_rot_out) {
+        Elem<T>::store(k_rot_out + in + kk, y1);
+        Elem<T>::store(k_rot_out + in + kk + half, y2);
+      }
+    } else {
+      Elem<T>::store(dst + kk, 0.f);
+      Elem<T>::store(dst + kk + half, 0.f);
+    }
+  }
+  if constexpr (TRANSPOSE_V) {
+    __shared__ uint16_t vs[TK][D + 2];
+    const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
+    for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
+      const int row = idx / D, d = idx - row * D;
+      const int j = j0 + row;
+      vs[row][d] = (j < L) ? vv[(((int64_t)b * L + j) * Hkv + g) * D + d] : (uint16_t)0;
+    }
+    __syncthreads();
+    const int ntiles = Lp / TK;
+    uint16_t* dst = vt + ((bg * ntiles + tile) * D) * TK;
+    for (int idx = threadIdx.x; idx < D * TK; idx += 256) {
+      const int d = idx / TK, p = idx - d * TK;
+      dst[idx] = vs[vt_perm(p)][d];
+    }
+  }
+}
+
+template <typename T, bool TV>
+static void launch_prep_t(int D, dim3 grid, hipStream_t st, const void* k, const void* v,
+                          const double2* table, void* krot, void* vt, void* k_rot_out, int L, int Lp,
+                          int Hkv, int s) {
+  if (D == 64)
+    hipLaunchKernelGGL((kv_prep_kernel<T, 64, TV>), grid, dim3(256), 0, st, (const T*)k, (const T*)v,
+                       table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, s);
+  else
+    hipLaunchKernelGGL((kv_prep_kernel<T, 128, TV>), grid, dim3(256), 0, st, (const T*)k,
+                       (const T*)v, table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, s);
+}
+
+hipError_t launch_kv_prep(const void* k, const void* v, const double2* table, void* krot, void* vt,
+                          void* k_rot_out, int64_t B, int64_t L, int64_t Lp, int64_t Hkv, int64_t D,
+                          int s, int dtype, hipStream_t st) {
+  const dim3 grid((unsigned)(Lp / kPrefillTileKeys), (unsigned)Hkv, (unsigned)B);
+  if (dtype == 0)
+    launch_prep_t<float, false>((int)D, grid, st, k, v, table, krot, vt, k_rot_out, (int)L, (int)Lp,
+                                (int)Hkv, s);
+  else
+    launch_prep_t<uint16_t, true>((int)D, grid, st, k, v, table, krot, vt, k_rot_out, (int)L,
+                                  (int)Lp, (int)Hkv, s);
+  return hipGetLastError();
+}
+
+}  // namespace dca

@@ -1,0 +1,163 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports every
+symbol include/dca.h declares, and rejects invalid calls before any HIP call.
+
+No call here passes validation, so nothing touches a device (the fake
+pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_dca_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dca.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+FAKE_WS = 0x100000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from long_context_attention_dca_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dca_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings_and_version(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.dca_status_string(code).decode().startswith("DCA_")
+    assert lib.dca_status_string(12345).decode() == "unknown DCA status"
+    assert lib.dca_version() == 10000
+
+
+def test_prefill_workspace_sizes(lib):
+    # fp32, B=1, L=512, Hkv=1, D=64, c=128: fp64 table 128*32*16 B, rotated keys 512*64*4 B.
+    assert lib.dca_prefill_workspace_bytes(1, 512, 1, 64, 128, 0) == 128 * 32 * 16 + 2 * 512 * 64 * 4
+    # plus the values (bf16: tiled transpose); L is padded to a multiple of 64 rows.
+    n = lib.dca_prefill_workspace_bytes(2, 100, 3, 128, 4096, 1)
+    assert n == 4096 * 64 * 16 + 2 * (2 * 3 * 128 * 128 * 2)
+    for bad in [(0, 512, 1, 64, 128, 0), (1, 0, 1, 64, 128, 0), (1, 512, 1, 96, 128, 0),
+                (1, 512, 1, 64, 128, 7), (1, 512, 0, 64, 128, 1)]:
+        assert lib.dca_prefill_workspace_bytes(*bad) == 0
+
+
+def test_decode_workspace_sizes(lib):
+    n = lib.dca_decode_workspace_bytes(16, 100001, 64, 8, 128, 1)
+    assert n > 16 * 64 * 3 * 128 * 2
+    assert n % 256 == 0
+    assert lib.dca_decode_workspace_bytes(1, 10, 6, 4, 128, 1) == 0   # Hq % Hkv
+    assert lib.dca_decode_workspace_bytes(1, 0, 8, 8, 128, 1) == 0
+
+
+PREFILL_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, k_rot_out=None, B=1, L=256, Hq=4, Hkv=2,
+                  D=128, c=128, w=32, base=10000.0, sm_scale=0.0, dtype=1, ws=FAKE_WS, ws_bytes=1 << 30,
+                  stream=None)
+
+
+def call_prefill(lib, **over):
+    a = dict(PREFILL_OK, **over)
+    return lib.dca_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["k_rot_out"], a["B"], a["L"],
+                           a["Hq"], a["Hkv"], a["D"], a["c"], a["w"], a["base"], a["sm_scale"],
+                           a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(v=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(o=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(D=96), _lib.DCA_ERR_UNSUPPORTED),
+    (dict(dtype=2), _lib.DCA_ERR_UNSUPPORTED),
+    (dict(w=128), _lib.DCA_ERR_INVALID_ARG),
+    (dict(w=-1), _lib.DCA_ERR_INVALID_ARG),
+    (dict(c=0, w=0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(Hq=3), _lib.DCA_ERR_INVALID_ARG),
+    (dict(L=0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(B=0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(base=0.0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(base=float("nan")), _lib.DCA_ERR_INVALID_ARG),
+    (dict(sm_scale=float("inf")), _lib.DCA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), _lib.DCA_ERR_INVALID_ARG),
+    (dict(k_rot_out=FAKE + 4), _lib.DCA_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.DCA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), _lib.DCA_ERR_WORKSPACE),
+    (dict(ws=FAKE_WS + 16), _lib.DCA_ERR_WORKSPACE),
+])
+def test_prefill_rejects_before_touching_device(lib, over, status):
+    assert call_prefill(lib, **over) == status
+
+
+DECODE_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, kv_len=1000, Hq=8, Hkv=2, D=64, c=128,
+                 w=32, base=10000.0, sm_scale=0.0, dtype=1, ws=FAKE_WS, ws_bytes=1 << 30, stream=None)
+
+
+def call_decode(lib, **over):
+    a = dict(DECODE_OK, **over)
+    return lib.dca_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["kv_len"], a["Hq"],
+                          a["Hkv"], a["D"], a["c"], a["w"], a["base"], a["sm_scale"], a["dtype"], a["ws"],
+                          a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(D=32), _lib.DCA_ERR_UNSUPPORTED),
+    (dict(w=200), _lib.DCA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.DCA_ERR_INVALID_ARG),
+    (dict(kv_len=0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), _lib.DCA_ERR_INVALID_ARG),
+    (dict(ws_bytes=0), _lib.DCA_ERR_WORKSPACE),
+])
+def test_decode_rejects_before_touching_device(lib, over, status):
+    assert call_decode(lib, **over) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, 1, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 1, 8, 2, 80, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, 1, 8, 2, 64, 0, 5, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 1, 8, 2, 64, -1, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 1, 8, 2, 64, 0, 0, 128, 128, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
+    ((FAKE, FAKE + 2, 1, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 0, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_OK),   # empty: no-op
+])
+def test_remap_validation(lib, args, status):
+    assert lib.dca_rope_remap(*args) == status
+
+
+def test_two_phase_prefill_validation(lib):
+    # prepare: k, v, k_rot_out, B, L, Hkv, D, c, w, base, dtype, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, None, 1, 256, 2, 128, 128, 32, 1e4, 1, FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(0, None, -1), (4, 0, -1), (6, 80, -2), (8, 128, -1), (9, -1.0, -1),
+                       (11, None, -3), (12, 16, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_prefill_prepare(*a) == st, (i, bad)
+    # attend: q, o, lse, B, L, Hq, Hkv, D, c, w, sm_scale, dtype, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, None, 1, 256, 4, 2, 128, 128, 32, 0.0, 1, FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(0, None, -1), (1, FAKE + 4, -1), (5, 3, -1), (7, 48, -2), (9, 200, -1),
+                       (10, float("nan"), -1), (12, None, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_prefill_attend(*a) == st, (i, bad)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "missing.so"))
