@@ -11,7 +11,11 @@
 // flash-attention tile costs; otherwise a straddling tile is processed once
 // per relation it contains, with the other relations' pairs masked out.
 //
-// bf16 kernel layout (one workgroup = 4 waves = 128 query rows of one head):
+// Two bf16 kernels share the tile math below: a two-group "ping-pong" kernel
+// used whenever the chunk size is a multiple of 64 (every (wave, tile) pair
+// has one relation), and a general kernel for any other chunk size.
+//
+// General bf16 kernel (one workgroup = 4 waves = 128 query rows of one head):
 //   * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
 //     wave's 32 rotated queries held in registers.  In the 32x32 output layout
 //     each lane owns one query column, so the row max / sum need a single
@@ -20,8 +24,9 @@
 //     and key-permuted by the prep pass), B = the probabilities straight from
 //     the S^T registers.
 //   * K and V^T tiles of 64 keys are double-buffered in LDS, filled by direct
-//     global->LDS loads (no staging registers) in XOR-swizzled 16-byte chunks
-//     so the MFMA fragment reads are conflict free; one barrier per tile.
+//     global->LDS loads (no staging registers); rows padded by 16 bytes make
+//     the MFMA fragment reads bank-conflict free with immediate offsets; one
+//     barrier per tile.
 //   * The query variant lives in registers and is re-made (rotate raw Q with the
 //     cos/sin table) only when the tile relation changes: inter -> successive
 //     -> intra, at most three times per workgroup on the fast path.
@@ -45,24 +50,26 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNoMax = -1.0e30f;  // running-max sentinel (finite)
 
-// 16-byte chunk swizzle for LDS tiles whose rows are NCK chunks long.
-template <int NCK>
-__device__ inline int swz(int row, int chunk) {
-  if constexpr (NCK == 16)
-    return chunk ^ (row & 15);
-  else
-    return chunk ^ ((row >> 1) & 7);
-}
-
+// LDS tiles.  Rows are padded by 16 bytes (K: 2D + 16, V^T: 2*64 + 16), which
+// spreads the 16 rows a quarter-wave reads over all 64 banks, and keeps every
+// fragment address of a tile a compile-time offset from one per-lane base.
+// Both tiles are whole multiples of 1 KiB, the unit of a direct-to-LDS load.
 template <int D>
 struct Smem {
-  static constexpr int KBYTES = BC * D * 2;
-  static constexpr int VBYTES = D * BC * 2;
+  static constexpr int KROW = D * 2 + 16;
+  static constexpr int VROW = BC * 2 + 16;
+  static constexpr int KBYTES = BC * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int KPIECES = KBYTES / 1024;
+  static constexpr int VPIECES = VBYTES / 1024;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int TOTAL = 2 * STAGE;
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole 1 KiB pieces");
 };
 
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ inline bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 // s_waitcnt vmcnt(0): this wave's global loads (including the direct-to-LDS
 // ones) have landed.  Encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
@@ -73,9 +80,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   constexpr int NDS = D / 16;          // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;          // 32-row blocks of O^T
-  constexpr int KCH = D / 8;           // 16-byte chunks per K row
-  constexpr int KLD = BC * KCH / 256;  // K chunks staged per thread per tile
-  constexpr int VLD = D * 8 / 256;     // V^T chunks staged per thread per tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<D>::TOTAL];
 
   // ---- work item ------------------------------------------------------------
@@ -151,34 +155,48 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   };
 
   // ---- K / V^T staging: direct global -> LDS loads ----------------------------
-  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS base + 16*l, so the
-  // swizzle is applied on the global side: the lane that lands on physical
-  // chunk p of a row fetches logical chunk swz(row, p) (the swizzle is an XOR,
-  // hence its own inverse).  Each wave issues a quarter of the 1-KB pieces.
-  constexpr int KPW = BC * D * 2 / 1024 / 4;  // K pieces per wave per tile
-  constexpr int VPW = D * BC * 2 / 1024 / 4;  // V^T pieces per wave per tile
+  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS base + 16*l: a wave
+  // fills one 1-KiB piece of the padded tile per instruction.  Each lane's
+  // source offset inside a tile is the same for every tile, so it is computed
+  // once; lanes that land on a row's 16-byte pad fetch that row's first chunk
+  // (a valid address; the pad is never read).  Pieces go round-robin to waves.
+  constexpr int KPW = (Smem<D>::KPIECES + 3) / 4;
+  constexpr int VPW = (Smem<D>::VPIECES + 3) / 4;
+  uint32_t koff[KPW], voff[VPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int byte = (wave + 4 * i) * 1024 + lane * 16;
+    const int row = byte / Smem<D>::KROW, w = byte % Smem<D>::KROW;
+    koff[i] = (uint32_t)(row * D * 2 + (w < D * 2 ? w : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) {
+    const int byte = (wave + 4 * i) * 1024 + lane * 16;
+    const int row = byte / Smem<D>::VROW, w = byte % Smem<D>::VROW;
+    voff[i] = (uint32_t)(row * BC * 2 + (w < BC * 2 ? w : 0));
+  }
   auto issue_tile = [&](int kt, int stage) {
-    const uint16_t* ks = kbase + (int64_t)kt * BC * D;
-    const uint16_t* vs = vbase + (int64_t)kt * BC * D;
+    const uint8_t* ks = (const uint8_t*)(kbase + (int64_t)kt * BC * D);
+    const uint8_t* vs = (const uint8_t*)(vbase + (int64_t)kt * BC * D);
     uint8_t* kb = smem + stage * Smem<D>::STAGE;
     uint8_t* vb = kb + Smem<D>::KBYTES;
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int r = wave * KPW + i;
-      const int byte = r * 1024 + lane * 16;
-      const int row = byte / (D * 2), pch = (byte % (D * 2)) / 16;
-      __builtin_amdgcn_global_load_lds((const void*)(ks + row * D + swz<KCH>(row, pch) * 8),
-                                       (__attribute__((address_space(3))) void*)(kb + r * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < KPW; ++i)
+      if (wave + 4 * i < Smem<D>::KPIECES)
+        __builtin_amdgcn_global_load_lds((const void*)(ks + koff[i]),
+                                         (__attribute__((address_space(3))) void*)(kb + (wave + 4 * i) * 1024),
+                                         16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-      const int r = wave * VPW + i;
-      const int byte = r * 1024 + lane * 16;
-      const int row = byte >> 7, pch = (byte & 127) >> 4;
-      __builtin_amdgcn_global_load_lds((const void*)(vs + row * BC + swz<8>(row, pch) * 8),
-                                       (__attribute__((address_space(3))) void*)(vb + r * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < VPW; ++i)
+      if (wave + 4 * i < Smem<D>::VPIECES)
+        __builtin_amdgcn_global_load_lds((const void*)(vs + voff[i]),
+                                         (__attribute__((address_space(3))) void*)(vb + (wave + 4 * i) * 1024),
+                                         16, 0, 0);
   };
+  // Per-lane fragment bases: K row (kb*32 + ql), V^T row (db*32 + ql); the
+  // lane's half hh selects the second 16 bytes of each 32-byte k-step.
+  const int kfrag = ql * Smem<D>::KROW + hh * 16;
+  const int vfrag = Smem<D>::KBYTES + ql * Smem<D>::VROW + hh * 16;
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -218,8 +236,8 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         // reads below are not hoisted out of this (rarely repeated) loop.
         int toff = stage * Smem<D>::STAGE;
         asm volatile("" : "+v"(toff));
-        const uint8_t* kb = smem + toff;
-        const uint8_t* vb = kb + Smem<D>::KBYTES;
+        const uint8_t* kb = smem + toff + kfrag;
+        const uint8_t* vb = smem + toff + vfrag;
         f32x16 sacc[2];
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
@@ -227,8 +245,7 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         for (int ds = 0; ds < NDS; ++ds) {
 #pragma unroll
           for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const int row = kb2 * 32 + ql, ch = ds * 2 + hh;
-            const bf16x8 kf = *(const bf16x8*)(kb + row * (D * 2) + swz<KCH>(row, ch) * 16);
+            const bf16x8 kf = *(const bf16x8*)(kb + kb2 * 32 * Smem<D>::KROW + ds * 32);
             sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb2], 0, 0, 0);
           }
         }
@@ -276,16 +293,19 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
           for (int u = 0; u < 2; ++u) {
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 8; ++e)
               p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][u * 8 + e], scale_log2, -m_run));
-              lsum += p[e];
-            }
-            const bf16x8 pf = as_bf16x8(pack_bf16x8(p));
+            const uint4 pu = pack_bf16x8(p);
+            // Row sum of the bf16-rounded probabilities (the values PV uses).
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, lsum, false);
+            const bf16x8 pf = as_bf16x8(pu);
             // ---- O^T += V^T P^T for this 16-key group ----
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              const int row = db * 32 + ql, ch = (kb2 * 2 + u) * 2 + hh;
-              const bf16x8 vf = *(const bf16x8*)(vb + row * 128 + swz<8>(row, ch) * 16);
+              const bf16x8 vf = *(const bf16x8*)(vb + db * 32 * Smem<D>::VROW + (kb2 * 2 + u) * 32);
               oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
             }
           }
@@ -310,6 +330,301 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         wv.x = pack_bf16x2(oacc[db][grp * 4] * inv, oacc[db][grp * 4 + 1] * inv);
         wv.y = pack_bf16x2(oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv);
         *(uint2*)(dst + db * 32 + grp * 8 + hh * 4) = wv;
+      }
+    if (hh == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---- bf16 ping-pong kernel (chunk size a multiple of 64) ------------------------
+// One workgroup = 8 waves = 256 query rows of one head.  Waves 0-3 (group 0)
+// and 4-7 (group 1) share the four SIMDs one-to-one and alternate, phase by
+// phase, between
+//   X(t): O^T += V(t-1)^T P(t-1)^T, then S^T(t) = K(t) Q^T    (32 MFMAs)
+//   Y(t): mask, row max, lazy rescale, exp, P(t) -> bf16      (VALU)
+// with group 1 one phase behind group 0, so each SIMD has one wave feeding the
+// matrix core while the other runs the softmax (the hardware co-issues them;
+// measured 4% faster than four independent waves per workgroup, and raising
+// the MFMA wave's priority made it slower).  Phases end at a workgroup
+// barrier.  K(t+1) and V(t) are loaded straight into LDS at the
+// start of phase 2t and waited for at the end of phase 2t+1; K and V are each
+// double-buffered.  With s a multiple of 64 every 32-row wave block lies in
+// one chunk and every 64-key tile in one chunk, so a (wave, tile) pair has a
+// single relation and no straddle handling is needed.
+constexpr int PP_BR = 256;
+
+// End of a phase: every LDS read of this wave has returned, then the
+// workgroup barrier.  Written as asm (with a compiler memory clobber) so the
+// compiler adds no wait on the direct-to-LDS loads still in flight, whose
+// data is only needed two phases later.
+__device__ inline void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<D>::TOTAL];
+  // LDS: K buffers 0/1 then V buffers 0/1.
+  constexpr int KB0 = 0, VB0 = 2 * Smem<D>::KBYTES;
+
+  // ---- work item (longest causal rows first, XCD-aware GQA grouping) ----------
+  const int wg = blockIdx.x;
+  int qt_rank, b, hq;
+  const int G = a.Hq / a.Hkv;
+  if (xcd_map) {
+    const int xcd = wg & 7, k = wg >> 3;
+    const int per_rank = (a.B * a.Hkv / 8) * G;
+    qt_rank = k / per_rank;
+    const int rem = k - qt_rank * per_rank;
+    const int slot = (rem / G) * 8 + xcd;
+    b = slot / a.Hkv;
+    hq = (slot - b * a.Hkv) * G + rem % G;
+  } else {
+    const int bh = a.B * a.Hq;
+    qt_rank = wg / bh;
+    const int rem = wg - qt_rank * bh;
+    b = rem / a.Hq;
+    hq = rem - b * a.Hq;
+  }
+  const int qt = nqt - 1 - qt_rank;
+  const int64_t bg = (int64_t)b * a.Hkv + hq / G;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
+  const int hh = lane >> 5, ql = lane & 31;
+  const int L = a.L, s = a.s, c = a.c;
+  const int i0 = qt * PP_BR;
+  const int i_lo = i0 + wave * 32;
+  const int qrow = i_lo + ql;
+  const int nq = i_lo / s;                 // the wave's 32 rows share one chunk
+  const int rq = qrow - nq * s;
+  const int nkt = min(i0 + PP_BR - 1, L - 1) / BC + 1;
+
+  const uint16_t* qsrc = (const uint16_t*)a.q + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+  const uint16_t* kbase = (const uint16_t*)a.krot + bg * (int64_t)a.Lp * D;
+  const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
+
+  bf16x8 qf[NDS];
+  auto load_q = [&](int cls) {
+    const int P = query_pos(cls, rq, s, c);
+    const double2* tb = a.table + (int64_t)P * (D / 2);
+    if (qrow < L) {
+#pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds) {
+        const uint4 u1 = *(const uint4*)(qsrc + ds * 16 + hh * 8);
+        const uint4 u2 = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
+        float x1[8], x2[8], y1[8], y2[8];
+        unpack_bf16x8(u1, x1);
+        unpack_bf16x8(u2, x2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double2 t = tb[ds * 16 + hh * 8 + e];
+          y1[e] = (float)((double)x1[e] * t.x - (double)x2[e] * t.y);
+          y2[e] = (float)((double)x2[e] * t.x + (double)x1[e] * t.y);
+        }
+        qf[ds] = as_bf16x8(pack_bf16x8(y1));
+        qf[ds + NDS / 2] = as_bf16x8(pack_bf16x8(y2));
+      }
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) qf[ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  };
+
+  // ---- direct-to-LDS staging, 1-KiB pieces round-robin over the 8 waves -----
+  constexpr int KPW = (Smem<D>::KPIECES + 7) / 8;
+  constexpr int VPW = (Smem<D>::VPIECES + 7) / 8;
+  uint32_t koff[KPW], voff[VPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int byte = (wave + 8 * i) * 1024 + lane * 16;
+    const int row = byte / Smem<D>::KROW, w = byte % Smem<D>::KROW;
+    koff[i] = (uint32_t)(row * D * 2 + (w < D * 2 ? w : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) {
+    const int byte = (wave + 8 * i) * 1024 + lane * 16;
+    const int row = byte / Smem<D>::VROW, w = byte % Smem<D>::VROW;
+    voff[i] = (uint32_t)(row * BC * 2 + (w < BC * 2 ? w : 0));
+  }
+  auto issue_k = [&](int kt) {
+    const uint8_t* src = (const uint8_t*)(kbase + (int64_t)kt * BC * D);
+    uint8_t* dst = smem + KB0 + (kt & 1) * Smem<D>::KBYTES;
+#pragma unroll
+    for (int i = 0; i < KPW; ++i)
+      if (wave + 8 * i < Smem<D>::KPIECES)
+        __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
+                                         (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
+                                         16, 0, 0);
+  };
+  auto issue_v = [&](int kt) {
+    const uint8_t* src = (const uint8_t*)(vbase + (int64_t)kt * BC * D);
+    uint8_t* dst = smem + VB0 + (kt & 1) * Smem<D>::VBYTES;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i)
+      if (wave + 8 * i < Smem<D>::VPIECES)
+        __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
+                                         (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
+                                         16, 0, 0);
+  };
+  const int kfrag = ql * Smem<D>::KROW + hh * 16;
+  const int vfrag = ql * Smem<D>::VROW + hh * 16;
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+  f32x16 sacc[2];
+  bf16x8 pf[4];
+  float m_run = kNoMax, l_run = 0.f;
+  int cur_cls = -1;
+
+  auto do_pv = [&](int t) {
+    const uint8_t* vb = smem + VB0 + (t & 1) * Smem<D>::VBYTES + vfrag;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 vf = *(const bf16x8*)(vb + db * 32 * Smem<D>::VROW + g4 * 32);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g4], oacc[db], 0, 0, 0);
+      }
+  };
+  auto do_qk = [&](int t) {
+    const uint8_t* kb = smem + KB0 + (t & 1) * Smem<D>::KBYTES + kfrag;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8 kf = *(const bf16x8*)(kb + kb2 * 32 * Smem<D>::KROW + ds * 32);
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb2], 0, 0, 0);
+      }
+  };
+  auto do_softmax = [&](int t) {
+    const int j0 = t * BC;
+    if (j0 + BC - 1 > i_lo) {   // tile reaches past the wave's first row: causal mask
+      const int jb = j0 + hh * 4;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = jb + kb2 * 32 + (v >> 2) * 8 + (v & 3);
+          sacc[kb2][v] = (j <= qrow) ? sacc[kb2][v] : -INFINITY;
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb2][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = mx * scale_log2;
+    if (__any(mnew > m_run + kRescaleThreshold)) {
+      const float mn = fmaxf(m_run, mnew);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+      m_run = mn;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g4 >> 1][(g4 & 1) * 8 + e], scale_log2, -m_run));
+      const uint4 pu = pack_bf16x8(p);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, lsum, false);
+      pf[g4] = as_bf16x8(pu);
+    }
+    l_run += lsum;
+  };
+
+  // ---- phases ---------------------------------------------------------------
+  // Both groups execute the same number of barriers; each runs its own loop
+  // so every iteration is straight-line code.  Tiles past a wave's last row
+  // are processed fully masked (p = 0) rather than skipped.
+  auto prep_q = [&](int t) {
+    const int cls = min(nq - (t * BC) / s, 2);
+    if (cls != cur_cls) {
+      load_q(cls);
+      cur_cls = cls;
+    }
+  };
+  // X(t) for 0 < t < nkt: PV(t-1) then QK(t), one straight-line block.
+  auto x_full = [&](int t) {
+    prep_q(t);
+    do_pv(t - 1);
+    do_qk(t);
+  };
+  issue_k(0);
+  wait_vmem();
+  phase_barrier();
+  // tile 0 (the first X phase has no PV; the last one, at t = nkt, has no QK)
+  if (nkt > 1) issue_k(1);
+  issue_v(0);
+  if (grp == 0) {
+    prep_q(0);
+    do_qk(0);
+    phase_barrier();
+    do_softmax(0);
+    wait_vmem();
+    phase_barrier();
+    for (int t = 1; t < nkt; ++t) {
+      if (t + 1 < nkt) issue_k(t + 1);
+      issue_v(t);
+      x_full(t);
+      phase_barrier();
+      do_softmax(t);
+      wait_vmem();
+      phase_barrier();
+    }
+    do_pv(nkt - 1);
+    phase_barrier();
+    phase_barrier();
+  } else {
+    phase_barrier();
+    prep_q(0);
+    do_qk(0);
+    wait_vmem();
+    phase_barrier();
+    for (int t = 1; t < nkt; ++t) {
+      if (t + 1 < nkt) issue_k(t + 1);
+      issue_v(t);
+      do_softmax(t - 1);
+      phase_barrier();
+      x_full(t);
+      wait_vmem();
+      phase_barrier();
+    }
+    do_softmax(nkt - 1);
+    phase_barrier();
+    do_pv(nkt - 1);
+    phase_barrier();
+  }
+
+  // ---- epilogue ----------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow < L) {
+    const float inv = 1.f / l_tot;
+    uint16_t* dst = (uint16_t*)a.o + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int grp4 = 0; grp4 < 4; ++grp4) {
+        uint2 wv;
+        wv.x = pack_bf16x2(oacc[db][grp4 * 4] * inv, oacc[db][grp4 * 4 + 1] * inv);
+        wv.y = pack_bf16x2(oacc[db][grp4 * 4 + 2] * inv, oacc[db][grp4 * 4 + 3] * inv);
+        *(uint2*)(dst + db * 32 + grp4 * 8 + hh * 4) = wv;
       }
     if (hh == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
   }
@@ -421,16 +736,24 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
-  const int nqt = (a.L + BR - 1) / BR;
-  const int64_t total = (int64_t)nqt * a.B * a.Hq;
   const int xcd_map = ((int64_t)a.B * a.Hkv) % 8 == 0 ? 1 : 0;
   const float scale_log2 = a.sm_scale * kLog2e;
+  if (a.s % BC == 0) {
+    // every wave block and key tile lies inside one chunk: ping-pong kernel
+    const int nqt = (a.L + PP_BR - 1) / PP_BR;
+    const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
+    if (a.D == 64)
+      hipLaunchKernelGGL(prefill_bf16_pp_kernel<64>, grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+    else
+      hipLaunchKernelGGL(prefill_bf16_pp_kernel<128>, grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+    return hipGetLastError();
+  }
+  const int nqt = (a.L + BR - 1) / BR;
+  const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
   if (a.D == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)total), dim3(256), 0, st, a, nqt,
-                       xcd_map, scale_log2);
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(256), 0, st, a, nqt, xcd_map, scale_log2);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)total), dim3(256), 0, st, a, nqt,
-                       xcd_map, scale_log2);
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(256), 0, st, a, nqt, xcd_map, scale_log2);
   return hipGetLastError();
 }
 

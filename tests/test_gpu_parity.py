@@ -118,6 +118,12 @@ SMALL = [
     ("bf16_L1", 1, 1, 2, 2, 128, 128, 32, torch.bfloat16, 2.0),
     ("bf16_L63", 3, 63, 2, 1, 64, 128, 32, torch.bfloat16, 2.0),
     ("bf16_L129", 1, 129, 4, 4, 128, 128, 64, torch.bfloat16, 2.0),
+    # chunk sizes that are multiples of 64 (the two-group kernel), ragged lengths
+    ("bf16_s64_d64_ragged", 2, 777, 4, 2, 64, 96, 32, torch.bfloat16, 2.0),
+    ("bf16_s128_w0_gqa", 1, 1000, 8, 2, 128, 128, 0, torch.bfloat16, 2.0),
+    ("bf16_s64_L1", 1, 1, 2, 1, 128, 64, 0, torch.bfloat16, 2.0),
+    ("bf16_s64_L300", 1, 300, 2, 2, 128, 100, 36, torch.bfloat16, 2.0),
+    ("bf16_s256_L257", 3, 257, 2, 1, 64, 320, 64, torch.bfloat16, 2.0),
 ]
 
 
