@@ -34,9 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DCA prefill TFLOP/s (% bf16 MFMA peak) at 32k/128k; decode GB/s (% HBM)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attend_llama2_70b_32k_traffic.json")
-KERNEL_SOURCES = ["long_context_attention_dca_amd/csrc/prefill.hip",
-                  "long_context_attention_dca_amd/csrc/dca_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama2_70b_32k_decode_100k.json")
 
 
 def log(msg):
@@ -53,25 +51,31 @@ def decode_bytes(B, kv_len, Hq, Hkv, D, esize=2):
     return B * kv_len * Hkv * D * esize * 2 + 2 * B * Hq * D * esize
 
 
-def kernel_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
-    or None when the kernel source changed since they were taken."""
+def measured_traffic(key):
+    """HBM bytes per launch of kernel `key` ("prefill_attend" or "decode_split")
+    from the committed rocprofv3 counter runs, or None when that kernel's source
+    changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            t = json.load(f)[key]
+        if t["source_sha256"] != source_hash(t["sources"]):
+            return None
+        return t["bytes_per_launch"]
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if t.get("source_sha256") != kernel_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+
+
+def prefill_kernel_name(c, w, D):
+    """The attention kernel the library launches for bf16 (chunk size s = c - w)."""
+    return f"prefill_bf16_pp_kernel<{D}>" if (c - w) % 64 == 0 else f"prefill_bf16_kernel<{D}>"
 
 
 def cpu_baseline(q, k, v, cfg, seconds):
@@ -215,10 +219,10 @@ def main():
         result["value"] = fl / ((prep_ms + att_ms) * 1e-3) / 1e12
         result["unit"] = "TFLOP/s"
         achieved = fl / (att_ms * 1e-3) / 1e12
-        traffic = measured_traffic()
         result["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                              "traffic": traffic, "kernel": "prefill_bf16_kernel<128>",
+                              "traffic": measured_traffic("prefill_attend"),
+                              "kernel": prefill_kernel_name(P["c"], P["w"], P["D"]),
                               "kernel_ms": att_ms, "flops_per_launch": fl}
         result["prefill_32k"] = {"ms": prep_ms + att_ms, "prepare_ms": prep_ms, "attend_ms": att_ms,
                                  "tflops": result["value"]}
@@ -227,7 +231,8 @@ def main():
         nb = decode_bytes(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"])
         gbps = nb / (dec_ms * 1e-3) / 1e9
         result["decode"] = {"ms": dec_ms, "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                            "frac": gbps / PEAK_HBM_GBPS, "bytes_per_call": nb, "bound": "hbm"}
+                            "frac": gbps / PEAK_HBM_GBPS, "bytes_per_call": nb, "bound": "hbm",
+                            "traffic": measured_traffic("decode_split")}
         if not run_prefill:
             result["value"], result["unit"] = gbps, "GB/s"
     cfg = {"workload": "llama2_70b_32k prefill + decode_100k" if run_prefill and run_decode else

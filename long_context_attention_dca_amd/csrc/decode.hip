@@ -12,11 +12,11 @@
 //   2. split   : each wave streams one contiguous key range of one (batch,
 //                KV head) and keeps an online softmax for the GQA group's query
 //                heads (up to 32 per pass, the N side of a 32x32 MFMA).  K and
-//                V rows are read with fully coalesced 16-byte loads; K goes to
-//                LDS as swizzled rows, V is transposed into LDS while being
-//                stored (16-bit stores), so both MFMA products read 16-byte
-//                fragments.  Partials (normalised O and log2-domain LSE) go to
-//                the workspace.
+//                V rows are read with fully coalesced 16-byte loads and stored
+//                to a per-wave LDS slice as rows (K XOR-swizzled, V padded);
+//                the PV operand V^T is read back with the transposing LDS read
+//                of gfx950, so no 16-bit scatter stores are needed.  Partials
+//                (normalised O and log2-domain LSE) go to the workspace.
 //   3. combine : log-sum-exp merge of the partials per query head.
 #include "dca_common.hpp"
 #include "dca_launch.hpp"
@@ -30,9 +30,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNoMax = -1.0e30f;  // running-max sentinel (finite)
 constexpr int SUB = 32;  // keys per wave sub-tile
+constexpr int kMaxSplits = 1024;  // partials merged per query head
 
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ inline int vt_perm(int p) { return (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
 template <int NCK>
 __device__ inline int swz(int row, int chunk) {
@@ -74,7 +74,10 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   constexpr int CPR = D / 8;             // 16-byte chunks per cache row
   constexpr int NI = SUB * CPR / 64;     // load instructions per sub-tile per tensor
   constexpr int KBYTES = SUB * D * 2;
-  constexpr int WBYTES = 2 * KBYTES;     // K rows + V^T, per wave
+  // V rows stay row-major in LDS, padded so that both the 16-byte row stores
+  // and the transposing fragment reads below are bank-conflict free.
+  constexpr int VROWB = D * 2 + 64;
+  constexpr int WBYTES = KBYTES + SUB * VROWB;  // K rows + V rows, per wave
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * WBYTES];
 
   const int lane = threadIdx.x & 63;
@@ -113,36 +116,52 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   };
 
   uint4 kreg[NI], vreg[NI];
-  auto gload = [&](int j0) {
+  auto gload_k = [&](int j0) {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int id = it * 64 + lane;
       const int row = id / CPR, ch = id % CPR;
       const int j = j0 + row;
-      if (j < kend) {
-        kreg[it] = *(const uint4*)(kc + (int64_t)j * row_stride + ch * 8);
-        vreg[it] = *(const uint4*)(vc + (int64_t)j * row_stride + ch * 8);
-      } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
-      }
+      kreg[it] = (j < kend) ? *(const uint4*)(kc + (int64_t)j * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto lstore = [&]() {
+  auto gload_v = [&](int j0) {
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int id = it * 64 + lane;
+      const int row = id / CPR, ch = id % CPR;
+      const int j = j0 + row;
+      vreg[it] = (j < kend) ? *(const uint4*)(vc + (int64_t)j * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore_k = [&]() {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int id = it * 64 + lane;
       const int row = id / CPR, ch = id % CPR;
       *(uint4*)(kl + row * (D * 2) + swz<CPR>(row, ch) * 16) = kreg[it];
-      const int p = vt_perm(row);
-      const uint32_t w[4] = {vreg[it].x, vreg[it].y, vreg[it].z, vreg[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = ch * 8 + e;
-        const uint16_t val = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
-        *(uint16_t*)(vl + d * 64 + swz<4>(d, p >> 3) * 16 + (p & 7) * 2) = val;
-      }
     }
+  };
+  auto lstore_v = [&]() {
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int id = it * 64 + lane;
+      const int row = id / CPR, ch = id % CPR;
+      *(uint4*)(vl + row * VROWB + ch * 16) = vreg[it];
+    }
+  };
+  // PV operand V^T from row-major V with ds_read_b64_tr_b16: inside each
+  // 16-lane group, lane s addresses key row (s / 4) and dims 4*(s % 4)..+3,
+  // and the instruction hands lane i four keys at dim i.  Two reads give a
+  // lane the 8 keys of its MFMA k-slots: keys hh*4 + 0..3 and 8 + hh*4 + 0..3
+  // of the 16-key group (the order the S^T output registers hold P in).
+  const int sl = lane & 15;
+  const int vtr = (hh * 4 + (sl >> 2)) * VROWB + ((((lane >> 4) & 1) * 16) + (sl & 3) * 4) * 2;
+  auto tr_read = [&](const uint8_t* base, int off) -> uint2 {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(base + off));
+    return __builtin_bit_cast(uint2, r);
   };
 
   f32x16 oacc[NDB];
@@ -153,12 +172,18 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   float m_run = kNoMax, l_run = 0.f;
   int cur_cls = -1;
 
-  gload(kbeg);
+  gload_k(kbeg);
+  gload_v(kbeg);
   for (int j0 = kbeg; j0 < kend; j0 += SUB) {
     __builtin_amdgcn_wave_barrier();
-    lstore();
+    // Store each half as soon as it lands and re-issue it at once, so the
+    // other half's loads stay in flight meanwhile.
+    const bool more = j0 + SUB < kend;
+    lstore_k();
+    if (more) gload_k(j0 + SUB);
+    lstore_v();
+    if (more) gload_v(j0 + SUB);
     __builtin_amdgcn_wave_barrier();
-    if (j0 + SUB < kend) gload(j0 + SUB);
 
     const int jl = min(j0 + SUB, kend) - 1;
     const int cls_lo = min(nq - jl / s, 2), cls_hi = min(nq - j0 / s, 2);
@@ -176,6 +201,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
       asm volatile("" : "+v"(toff));
       const uint8_t* kl = smem + toff;
       const uint8_t* vl = kl + KBYTES;
+      const uint8_t* vtb = vl + vtr;
       f32x16 sacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
@@ -228,8 +254,9 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
         const bf16x8 pf = as_bf16x8(pack_bf16x8(p));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + ql;
-          const bf16x8 vf = *(const bf16x8*)(vl + d * 64 + swz<4>(d, u * 2 + hh) * 16);
+          const uint2 lo = tr_read(vtb, u * 16 * VROWB + db * 64);
+          const uint2 hi = tr_read(vtb, u * 16 * VROWB + 8 * VROWB + db * 64);
+          const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
         }
       }
@@ -319,21 +346,40 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
 
 // ---- 3. combine ----------------------------------------------------------------------
 template <typename T>
-__global__ void decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                      T* __restrict__ o, float* __restrict__ lse, int D, int ns) {
-  const int bh = blockIdx.x, d = threadIdx.x;
+__global__ void __launch_bounds__(128) decode_combine_kernel(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_lse,
+                                                             T* __restrict__ o, float* __restrict__ lse, int D,
+                                                             int ns) {
+  // One workgroup per (batch, query head): the split weights 2^(lse_i - M)
+  // are computed once into LDS, then every thread sums one output dim.
+  __shared__ float wts[kMaxSplits];
+  __shared__ float red[2];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const float* pl = part_lse + (int64_t)bh * ns;
   float M = -INFINITY;
-  for (int i = 0; i < ns; ++i) M = fmaxf(M, pl[i]);
-  float wsum = 0.f, acc = 0.f;
-  const float* po = part_o + (int64_t)bh * ns * D;
-  for (int i = 0; i < ns; ++i) {
+  for (int i = tid; i < ns; i += 128) M = fmaxf(M, pl[i]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float ws = 0.f;
+  for (int i = tid; i < ns; i += 128) {
     const float wgt = exp2f(pl[i] - M);
-    wsum += wgt;
-    if (d < D) acc = fmaf(wgt, po[(int64_t)i * D + d], acc);
+    wts[i] = wgt;
+    ws += wgt;
   }
-  if (d < D) Elem<T>::store(o + (int64_t)bh * D + d, acc / wsum);
-  if (d == 0 && lse) lse[bh] = (M + log2f(wsum)) * kLn2;
+  for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = ws;
+  __syncthreads();
+  const float wsum = red[0] + red[1];
+  if (tid < D) {
+    const float* po = part_o + (int64_t)bh * ns * D + tid;
+    float acc = 0.f;
+    for (int i = 0; i < ns; ++i) acc = fmaf(wts[i], po[(int64_t)i * D], acc);
+    Elem<T>::store(o + (int64_t)bh * D + tid, acc / wsum);
+  }
+  if (tid == 0 && lse) lse[bh] = (M + log2f(wsum)) * kLn2;
 }
 
 }  // namespace
@@ -342,11 +388,18 @@ void decode_plan(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int dtype, 
                  int* nsplit) {
   const int64_t G = Hq / Hkv;
   const int64_t units = dtype == 0 ? B * Hq : B * Hkv * ((G + 31) / 32);
-  const int64_t target = dtype == 0 ? 2048 : 8192;  // concurrent workers to aim for
+  // One wave per split, as many splits as the chip holds at once: MI355X runs
+  // 8 of these waves per CU (2 per SIMD) on 256 CUs.  One round of long splits
+  // measured faster than several rounds of short ones (fewer prologues,
+  // partials and round boundaries).
+  const int64_t target = 2048;
   int64_t per = (target + units - 1) / units;
   if (per < 1) per = 1;
   int64_t kps = (kv_len + per - 1) / per;
-  kps = round_up(kps < 256 ? 256 : kps, SUB);
+  kps = kps < 256 ? 256 : kps;
+  // the combine kernel keeps one weight per split in LDS: at most kMaxSplits
+  const int64_t min_kps = (kv_len + kMaxSplits - 1) / kMaxSplits;
+  kps = round_up(kps < min_kps ? min_kps : kps, SUB);
   *keys_per_split = (int)kps;
   *nsplit = (int)((kv_len + kps - 1) / kps);
 }
