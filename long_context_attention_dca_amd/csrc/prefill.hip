@@ -351,6 +351,9 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 // one chunk and every 64-key tile in one chunk, so a (wave, tile) pair has a
 // single relation and no straddle handling is needed.
 constexpr int PP_BR = 256;
+// Word 3 of a raw buffer descriptor on gfx9-family parts (gfx950): 32-bit
+// data format, no swizzle, offsets bounded by the record count in word 2.
+constexpr int kBufferWord3 = 0x00020000;
 
 // End of a phase: every LDS read of this wave has returned, then the
 // workgroup barrier.  Written as asm (with a compiler memory clobber) so the
@@ -448,25 +451,30 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     const int row = byte / Smem<D>::VROW, w = byte % Smem<D>::VROW;
     voff[i] = (uint32_t)(row * BC * 2 + (w < BC * 2 ? w : 0));
   }
+  // K/V tiles go straight to LDS through buffer loads (MUBUF with the lds
+  // bit).  The descriptor covers this head's Lp rows exactly.  The FLAT form
+  // of the same DMA would make the compiler wait for every outstanding LDS
+  // read (lgkmcnt(0)) while it is in flight.
+  const uint32_t head_bytes = (uint32_t)((int64_t)a.Lp * D * 2);
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, kBufferWord3);
   auto issue_k = [&](int kt) {
-    const uint8_t* src = (const uint8_t*)(kbase + (int64_t)kt * BC * D);
+    const int soff = kt * BC * D * 2;
     uint8_t* dst = smem + KB0 + (kt & 1) * Smem<D>::KBYTES;
 #pragma unroll
     for (int i = 0; i < KPW; ++i)
       if (wave + 8 * i < Smem<D>::KPIECES)
-        __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
-                                         (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
+                                                 16, (int)koff[i], soff, 0, 0);
   };
   auto issue_v = [&](int kt) {
-    const uint8_t* src = (const uint8_t*)(vbase + (int64_t)kt * BC * D);
+    const int soff = kt * BC * D * 2;
     uint8_t* dst = smem + VB0 + (kt & 1) * Smem<D>::VBYTES;
 #pragma unroll
     for (int i = 0; i < VPW; ++i)
       if (wave + 8 * i < Smem<D>::VPIECES)
-        __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
-                                         (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
+                                                 16, (int)voff[i], soff, 0, 0);
   };
   const int kfrag = ql * Smem<D>::KROW + hh * 16;
   const int vfrag = ql * Smem<D>::VROW + hh * 16;
@@ -549,6 +557,12 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     l_run += lsum;
   };
 
+  // The probabilities feed the next phase's PV product; without this the
+  // compiler sinks their exps past the phase barrier, next to that use.
+  auto pin_p = [&]() {
+    asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
+  };
+
   // ---- phases ---------------------------------------------------------------
   // Both groups execute the same number of barriers; each runs its own loop
   // so every iteration is straight-line code.  Tiles past a wave's last row
@@ -560,11 +574,47 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
       cur_cls = cls;
     }
   };
-  // X(t) for 0 < t < nkt: PV(t-1) then QK(t), one straight-line block.
+  // X(t) for 0 < t < nkt: PV(t-1) then QK(t) as one chain of 32 MFMAs whose
+  // LDS operands are read NPRE fragments ahead (a ring of registers), so each
+  // MFMA waits only for the oldest read in flight.
   auto x_full = [&](int t) {
     prep_q(t);
-    do_pv(t - 1);
-    do_qk(t);
+    constexpr int NPV = 4 * NDB, NQK = 2 * NDS, NX = NPV + NQK, NPRE = 6;
+    const uint8_t* vb = smem + VB0 + ((t - 1) & 1) * Smem<D>::VBYTES + vfrag;
+    const uint8_t* kb = smem + KB0 + (t & 1) * Smem<D>::KBYTES + kfrag;
+    auto frag = [&](int i) -> bf16x8 {
+      if (i < NPV) {
+        const int g4 = i / NDB, db = i % NDB;
+        return *(const bf16x8*)(vb + db * 32 * Smem<D>::VROW + g4 * 32);
+      }
+      const int ds = (i - NPV) / 2, kb2 = (i - NPV) % 2;
+      return *(const bf16x8*)(kb + kb2 * 32 * Smem<D>::KROW + ds * 32);
+    };
+    bf16x8 ring[NPRE];
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) ring[i] = frag(i);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const bf16x8 f = ring[i % NPRE];
+      if (i + NPRE < NX) ring[i % NPRE] = frag(i + NPRE);
+      if (i < NPV) {
+        const int g4 = i / NDB, db = i % NDB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[g4], oacc[db], 0, 0, 0);
+      } else {
+        const int ds = (i - NPV) / 2, kb2 = (i - NPV) % 2;
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[ds], sacc[kb2], 0, 0, 0);
+      }
+    }
+    // Order: NPRE reads, then (MFMA, read) pairs, then the last MFMAs.
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + NPRE < NX) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
   issue_k(0);
   wait_vmem();
@@ -601,6 +651,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
       if (t + 1 < nkt) issue_k(t + 1);
       issue_v(t);
       do_softmax(t - 1);
+      pin_p();
       phase_barrier();
       x_full(t);
       wait_vmem();
