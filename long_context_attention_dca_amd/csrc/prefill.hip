@@ -350,7 +350,23 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 // double-buffered.  With s a multiple of 64 every 32-row wave block lies in
 // one chunk and every 64-key tile in one chunk, so a (wave, tile) pair has a
 // single relation and no straddle handling is needed.
+// Maximum of a lane's 32 scores as a tree of max3 (depth 4), so the wave is
+// not held up by a 16-deep dependency chain.
+__device__ inline float max32(const f32x16 (&x)[2]) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int a = 3 * i, b = a + 1, c = a + 2;
+    t[i] = fmaxf(fmaxf(x[a >> 4][a & 15], x[b >> 4][b & 15]), x[c >> 4][c & 15]);
+  }
+  t[10] = fmaxf(x[1][14], x[1][15]);
+  const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+  const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
+  return fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+}
+
 constexpr int PP_BR = 256;
+constexpr float kSumLimit = 256.0f;  // per-lane probability sum that forces a rescale
 // Word 3 of a raw buffer descriptor on gfx9-family parts (gfx950): 32-bit
 // data format, no swizzle, offsets bounded by the record count in word 2.
 constexpr int kBufferWord3 = 0x00020000;
@@ -523,14 +539,31 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
           sacc[kb2][v] = (j <= qrow) ? sacc[kb2][v] : -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    // Probabilities against the running max first.  A lane whose 32
+    // probabilities sum past 2^8 (or to inf on the first tile, where the
+    // running max is the sentinel) sends the wave through the exact rescale:
+    // the true max, the accumulator rescale and the exps again.  Every stored
+    // probability is therefore at most 2^8 and O and l share one max.
+    auto exps = [&]() {
+      float lsum[4];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float p[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb2][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = mx * scale_log2;
-    if (__any(mnew > m_run + kRescaleThreshold)) {
+        for (int e = 0; e < 8; ++e)
+          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g4 >> 1][(g4 & 1) * 8 + e], scale_log2, -m_run));
+        const uint4 pu = pack_bf16x8(p);
+        float ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, 0.f, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, ls, false);
+        lsum[g4] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, ls, false);
+        pf[g4] = as_bf16x8(pu);
+      }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    float lt = exps();
+    if (__any(!(lt <= kSumLimit))) {
+      const float mnew = max_halves(max32(sacc)) * scale_log2;
       const float mn = fmaxf(m_run, mnew);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
       l_run *= alpha;
@@ -539,22 +572,9 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
       m_run = mn;
+      lt = exps();
     }
-    float lsum = 0.f;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g4 >> 1][(g4 & 1) * 8 + e], scale_log2, -m_run));
-      const uint4 pu = pack_bf16x8(p);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, lsum, false);
-      pf[g4] = as_bf16x8(pu);
-    }
-    l_run += lsum;
+    l_run += lt;
   };
 
   // The probabilities feed the next phase's PV product; without this the
@@ -664,7 +684,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (qrow < L) {
     const float inv = 1.f / l_tot;
     uint16_t* dst = (uint16_t*)a.o + (((int64_t)b * L + qrow) * a.Hq + hq) * D;

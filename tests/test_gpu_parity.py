@@ -188,6 +188,35 @@ def test_prefill_planted_keys(dtype, case):
         assert np.abs(o[0, i, 0] - want).max() <= F32_TOL
 
 
+# Chunk size a multiple of 64 (the two-group kernel) and a planted logit of 12:
+# the planted probability is about 2^17 times the others, far past the
+# per-lane sum that forces the running max to move at a later key tile.
+PLANTED_RESCALE = {
+    "succ_exact_s128": (192, 64, 300, 200),   # rho 1, r(i) = 44 < w
+    "inter_s128": (192, 64, 700, 150),        # rho 4
+}
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", sorted(PLANTED_RESCALE))
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_planted_rescale(dtype, case, D):
+    from test_oracle_pins import planted_case
+    c, w, i, jstar = PLANTED_RESCALE[case]
+    q, k, v, want = planted_case(c, w, i, jstar, D=D, seed=4, target_logit=12.0)
+    L = i + 70
+    pad = lambda x: np.concatenate([x, np.random.default_rng(2).standard_normal((1, 70, 1, D)) * 0.1], 1)
+    qt, kt, vt = (torch.from_numpy(pad(x)).to(dtype) for x in (q, k, v))
+    o, lse = dca.prefill(qt.to(dev()), kt.to(dev()), vt.to(dev()), c, w, 1e4, return_lse=True)
+    O, LSE = oracle.dca_prefill_ref(qt, kt, vt, c, w, 1e4, rows=[i])
+    assert_close(to_np(o)[:, i], O[:, 0], dtype, case)
+    bound = lse_bound_prefill(qt, kt, dtype)
+    bound = bound if np.isscalar(bound) else bound[0, 0, i]
+    assert abs(to_np(lse)[0, 0, i] - LSE[0, 0, 0]) <= bound
+    if dtype == torch.float32:
+        assert np.abs(to_np(o)[0, i, 0] - want).max() <= F32_TOL
+
+
 def test_prefill_deterministic_and_causal():
     B, L, Hq, Hkv, D, c, w = 1, 777, 4, 1, 128, 256, 64
     q, k, v = (x.to(dev()) for x in inputs.prefill_inputs(B, L, Hq, Hkv, D, "bf16", seed=9, qk_scale=2.0))
