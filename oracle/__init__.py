@@ -23,3 +23,17 @@ from .dca_ref import (  # noqa: F401
     MAP_Q_INTER,
     MAP_PLAIN,
 )
+from .selfextend_ref import (  # noqa: F401
+    MAP_SE_KEY_GROUPED,
+    MAP_SE_Q_GROUPED,
+    NEIGHBOR,
+    GROUPED,
+    se_relation,
+    se_key_position,
+    se_query_position,
+    se_relative_position_table,
+    se_remap_positions,
+    se_rope_remap_ref,
+    selfextend_prefill_ref,
+    selfextend_prefill_formB,
+)
