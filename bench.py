@@ -115,7 +115,8 @@ def main():
     ap.add_argument("--no-128k", action="store_true", help="skip the 131072-token prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k"], default=None,
+    ap.add_argument("--no-selfextend", action="store_true", help="skip the SelfExtend 32k prefill")
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k", "selfextend"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
@@ -150,6 +151,8 @@ def main():
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode")
     run_128k = (args.only == "prefill128k") or (args.only is None and not args.no_128k)
+    SE = inputs.WORKLOADS["selfextend_70b_32k"]
+    run_se = (args.only == "selfextend") or (args.only is None and not args.no_selfextend)
 
     # ---------------- inputs, resident in HBM before timing ----------------
     if run_prefill:
@@ -240,6 +243,42 @@ def main():
            "prefill": {k_: P[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")},
            "decode": {k_: DC[k_] for k_ in ("B", "kv_len", "Hq", "Hkv", "D", "c", "w")}}
     result["config"] = cfg
+
+    # ---------------- SelfExtend 32k prefill (reported beside the step) ---------
+    if run_se:
+        log("generating selfextend_70b_32k inputs")
+        sq_h, sk_h, sv_h = inputs.prefill_inputs(SE["B"], SE["L"], SE["Hq"], SE["Hkv"], SE["D"], "bf16",
+                                                 SE["seed"])
+        sq, sk, sv = sq_h.to(dev), sk_h.to(dev), sv_h.to(dev)
+        del sq_h, sk_h, sv_h
+        sws = torch.empty(dca.selfextend_workspace_bytes(SE["B"], SE["L"], SE["Hkv"], SE["D"], SE["group"],
+                                                         SE["window"], torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        se_call = lambda: dca.selfextend_prefill(sq, sk, sv, SE["group"], SE["window"], SE["base"],
+                                                 workspace=sws)
+        for _ in range(max(1, args.warmup)):
+            se_call()
+        torch.cuda.synchronize()
+        nse = max(1, min(args.steps, 5))
+        sev = [events(2) for _ in range(nse)]
+        for i in range(nse):
+            sev[i][0].record()
+            se_call()
+            sev[i][1].record()
+        torch.cuda.synchronize()
+        se_ms = sum(e[0].elapsed_time(e[1]) for e in sev) / nse
+        fl = prefill_flops(SE["B"], SE["L"], SE["Hq"], SE["D"])
+        result["selfextend_32k"] = {"ms": se_ms, "tflops": fl / (se_ms * 1e-3) / 1e12,
+                                    "frac": fl / (se_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                    "group": SE["group"], "window": SE["window"], "steps": nse,
+                                    "includes": "cos/sin table, both key rotations, V layout, attention"}
+        if args.only == "selfextend":
+            result["value"], result["unit"] = result["selfextend_32k"]["tflops"], "TFLOP/s"
+            result["config"] = {"workload": "selfextend_70b_32k",
+                                "prefill": {k_: SE[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "group",
+                                                                  "window")}}
+        del sq, sk, sv, sws
+        torch.cuda.empty_cache()
 
     # ---------------- 128k prefill (reported beside the step) ----------------
     if run_128k:

@@ -56,10 +56,15 @@ extern "C" {
 #define DCA_MAP_Q_SUCC 2  /* P = min(s + (t mod s), c - 1)    */
 #define DCA_MAP_Q_INTER 3 /* P = c - 1                        */
 #define DCA_MAP_PLAIN 4   /* P = t (ordinary RoPE)            */
+/* SelfExtend grouped positions (see dca_selfextend_prefill); for these two maps
+ * the (c, w) arguments carry the group size G >= 1 and the window W >= 0.     */
+#define DCA_MAP_SE_KEY_GROUPED 5 /* P = floor(t / G)                    */
+#define DCA_MAP_SE_Q_GROUPED 6   /* P = floor(t / G) + W - floor(W / G) */
 
 /* Status codes. */
 #define DCA_OK 0
-#define DCA_ERR_INVALID_ARG (-1) /* null pointer, bad shape, w >= c, Hq % Hkv != 0, misalignment */
+#define DCA_ERR_INVALID_ARG (-1) /* null pointer, bad shape, w >= c, Hq % Hkv != 0, misalignment,
+                                    SelfExtend group < 1 or window < 0                          */
 #define DCA_ERR_UNSUPPORTED (-2) /* head dim or dtype the kernels do not implement               */
 #define DCA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the query returned          */
 #define DCA_ERR_HIP (-4)         /* a HIP launch reported an error                                */
@@ -84,7 +89,9 @@ int dca_version(void);
  *
  *   x, out : [B, L, H, D] of `dtype`, device; out may equal x (in place).
  *   pos0   : >= 0, position of token 0.
- *   map    : one of DCA_MAP_*.
+ *   map    : one of DCA_MAP_*.  For DCA_MAP_SE_KEY_GROUPED / DCA_MAP_SE_Q_GROUPED
+ *            c is the SelfExtend group size G (1 <= G <= 2^24) and w the
+ *            window W (0 <= W <= 2^30); the DCA rule w < c does not apply.
  * Angles, cos/sin and the rotation are evaluated in fp64; the result is
  * rounded to nearest even into the output type (bf16 through fp32).
  */
@@ -150,6 +157,43 @@ int dca_prefill_prepare(const void* k, const void* v, void* k_rot_out, int64_t B
 int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L, int64_t Hq,
                        int64_t Hkv, int64_t D, int c, int w, float sm_scale, int dtype,
                        const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * SelfExtend-style grouped / neighbor attention through the same prefill
+ * kernels.
+ *
+ * Definition: "LLM Maybe LongLM: Self-Extend LLM Context Window Without
+ * Tuning" (abstract) builds two levels of attention from the model's own
+ * attention: grouped attention for distant tokens and neighbor attention for
+ * tokens within a window.  The abstract states no formula; the positions used
+ * are (for causal pairs j <= i, group size G, window W):
+ *   i - j <  W (neighbor): query at i, key at j (ordinary RoPE);
+ *   i - j >= W (grouped) : query at floor(i/G) + W - floor(W/G), key at
+ *                          floor(j/G) -- the grouped distance continues the
+ *                          window edge and is never below W.
+ * Softmax, scale, LSE, GQA, layouts and dtypes as in dca_prefill.
+ *
+ * dca_selfextend_workspace_bytes: scratch bytes for these sizes (0 on invalid
+ * sizes): the fp64 cos/sin table for every position used, the keys rotated at
+ * j and at floor(j/G) (head-major, rows padded to a multiple of 64) and the
+ * value layout (bf16: tiled transpose; fp32: a copy).
+ *
+ * dca_selfextend_prefill:
+ *   q      : [B, L, Hq, D] raw queries; k, v : [B, L, Hkv, D] raw keys, values.
+ *   o      : [B, L, Hq, D] output; lse : [B, Hq, L] fp32 or NULL.
+ *   group  : G >= 1 (G = 1 is ordinary RoPE attention); window : W >= 0
+ *            (W >= L is ordinary RoPE attention; W = 0 groups every pair).
+ *   ws     : scratch of at least dca_selfextend_workspace_bytes(...) bytes.
+ * Key tiles holding grouped pairs and those holding neighbor pairs are visited
+ * in turn; tiles on the window edge twice, each time with the other class
+ * masked, merged by the online softmax.
+ */
+size_t dca_selfextend_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int group,
+                                      int window, int dtype);
+int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int group,
+                           int window, double rope_base, float sm_scale, int dtype, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * Scratch bytes dca_decode needs for these sizes (0 on invalid sizes): the

@@ -12,7 +12,10 @@ Entry points (same names as include/dca.h):
           return_k_rot=False, workspace=None)
   decode(q, k_cache, v_cache, c, w, base=1e4, sm_scale=None,
          return_lse=False, workspace=None)
-  prefill_workspace_bytes(...), decode_workspace_bytes(...)
+  selfextend_prefill(q, k, v, group, window, base=1e4, sm_scale=None,
+                     return_lse=False, workspace=None)
+  prefill_workspace_bytes(...), decode_workspace_bytes(...),
+  selfextend_workspace_bytes(...)
 """
 from __future__ import annotations
 
@@ -21,11 +24,12 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     DCA_BF16, DCA_F32, DCA_MAP_KEY, DCA_MAP_PLAIN, DCA_MAP_Q_INTER, DCA_MAP_Q_INTRA,
-    DCA_MAP_Q_SUCC, DCAError,
+    DCA_MAP_Q_SUCC, DCA_MAP_SE_KEY_GROUPED, DCA_MAP_SE_Q_GROUPED, DCAError,
 )
 
 __all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
-           "prefill_workspace_bytes", "decode_workspace_bytes", "DCAError", "library_path"]
+           "selfextend_prefill", "prefill_workspace_bytes", "decode_workspace_bytes",
+           "selfextend_workspace_bytes", "DCAError", "library_path"]
 
 _DT = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}
 
@@ -71,6 +75,11 @@ def decode_workspace_bytes(B, kv_len, Hq, Hkv, D, dtype) -> int:
     return int(_lib.load().dca_decode_workspace_bytes(B, kv_len, Hq, Hkv, D, code))
 
 
+def selfextend_workspace_bytes(B, L, Hkv, D, group, window, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(_lib.load().dca_selfextend_workspace_bytes(B, L, Hkv, D, group, window, code))
+
+
 def _workspace(nbytes: int, device, workspace):
     if workspace is None:
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -81,7 +90,8 @@ def _workspace(nbytes: int, device, workspace):
 
 def rope_remap(x: torch.Tensor, map: int, c: int, w: int, base: float = 10000.0, pos0: int = 0,
                out: torch.Tensor | None = None) -> torch.Tensor:
-    """Rotate x [B, L, H, D] by the DCA position map `map` (token t at pos0 + t)."""
+    """Rotate x [B, L, H, D] by position map `map` (token t at pos0 + t).  For the
+    SelfExtend grouped maps, c is the group size and w the window."""
     lib = _lib.load()
     _check(x, "x", 4)
     if out is None:
@@ -184,5 +194,31 @@ def decode(q, k_cache, v_cache, c: int, w: int, base: float = 10000.0, sm_scale:
     _lib.check("dca_decode", lib.dca_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), _ptr(lse),
         B, kv_len, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def selfextend_prefill(q, k, v, group: int, window: int, base: float = 10000.0,
+                       sm_scale: float | None = None, return_lse: bool = False, workspace=None):
+    """SelfExtend grouped / neighbor causal prefill.  q [B, L, Hq, D], k/v [B, L, Hkv, D] raw;
+    returns o (and lse)."""
+    lib = _lib.load()
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, L, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    code = _dtype_code(q)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, L, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(lib.dca_selfextend_workspace_bytes(B, L, Hkv, D, group, window, code))
+    if nbytes == 0:
+        raise ValueError("invalid SelfExtend prefill sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_selfextend_prefill", lib.dca_selfextend_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+        B, L, Hq, Hkv, D, group, window, float(base), float(sm_scale or 0.0), code,
         ws.data_ptr(), nbytes, _stream(q.device)))
     return (o, lse) if return_lse else o

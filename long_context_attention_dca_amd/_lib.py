@@ -15,6 +15,8 @@ DCA_MAP_Q_INTRA = 1
 DCA_MAP_Q_SUCC = 2
 DCA_MAP_Q_INTER = 3
 DCA_MAP_PLAIN = 4
+DCA_MAP_SE_KEY_GROUPED = 5
+DCA_MAP_SE_Q_GROUPED = 6
 DCA_OK = 0
 DCA_ERR_INVALID_ARG = -1
 DCA_ERR_UNSUPPORTED = -2
@@ -37,6 +39,9 @@ SIGNATURES = {
                                    _sz, _vp]),
     "dca_prefill_attend": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _flt, _int,
                                   _vp, _sz, _vp]),
+    "dca_selfextend_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _int]),
+    "dca_selfextend_prefill": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int,
+                                      _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
     "dca_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _dbl,
                           _flt, _int, _vp, _sz, _vp]),

@@ -45,6 +45,35 @@ bool prefill_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c, int dty
   return true;
 }
 
+// SelfExtend workspace: fp64 cos/sin table for positions [0, npos) | keys at j
+// | keys at floor(j / G) | V (bf16: tiled transpose; fp32: copy).
+bool se_ok(int64_t G, int64_t W) { return G >= 1 && G <= (1 << 24) && W >= 0 && W <= (1 << 30); }
+
+struct SeLayout {
+  int64_t Lp, npos;
+  size_t table, krot, krot2, vt, total;
+};
+
+bool se_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int G, int W, int dtype, SeLayout* out) {
+  if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype) || !se_ok(G, W)) return false;
+  if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
+  SeLayout p;
+  p.Lp = round_up(L, kPrefillTileKeys);
+  // largest position used: L - 1 (neighbor query) or the grouped query of row L - 1
+  const int64_t top_grouped = (L - 1) / G + W - W / G;
+  p.npos = (top_grouped > L - 1 ? top_grouped : L - 1) + 1;
+  if (p.npos >= kMaxDim / 64) return false;
+  const int64_t tbytes = p.npos * (D / 2) * 16;
+  const int64_t kbytes = B * Hkv * p.Lp * D * elem_size(dtype);
+  p.table = 0;
+  p.krot = (size_t)round_up(tbytes, 256);
+  p.krot2 = p.krot + (size_t)round_up(kbytes, 256);
+  p.vt = p.krot2 + (size_t)round_up(kbytes, 256);
+  p.total = p.vt + (size_t)round_up(kbytes, 256);
+  *out = p;
+  return true;
+}
+
 struct DecodeLayout {
   int kps, ns;
   size_t qv, part_o, part_lse, total;
@@ -95,8 +124,9 @@ int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, in
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!x || !out || B < 0 || L < 0 || H < 0 || pos0 < 0) return DCA_ERR_INVALID_ARG;
   if (B >= kMaxDim || L >= kMaxDim || H >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
-  if (!cw_ok(c, w) || map < DCA_MAP_KEY || map > DCA_MAP_PLAIN || !base_ok(rope_base))
-    return DCA_ERR_INVALID_ARG;
+  const bool se_map = map == DCA_MAP_SE_KEY_GROUPED || map == DCA_MAP_SE_Q_GROUPED;
+  if (map < DCA_MAP_KEY || map > DCA_MAP_SE_Q_GROUPED || !base_ok(rope_base)) return DCA_ERR_INVALID_ARG;
+  if (se_map ? !se_ok(c, w) : !cw_ok(c, w)) return DCA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(out, 16)) return DCA_ERR_INVALID_ARG;
   if (B == 0 || L == 0 || H == 0) return DCA_OK;
   return hip_status(launch_rope_remap(x, out, B, L, H, D, pos0, map, c, w, rope_base, dtype,
@@ -124,7 +154,7 @@ static int prepare_impl(const void* k, const void* v, void* k_rot_out, int64_t B
   double2* table = (double2*)(base + p.table);
   hipError_t e = launch_rope_table(table, c, (int)D, rope_base, st);
   if (e != hipSuccess) return DCA_ERR_HIP;
-  e = launch_kv_prep(k, v, table, base + p.krot, base + p.vt, k_rot_out, B, L, p.Lp, Hkv, D, c - w,
+  e = launch_kv_prep(k, v, table, base + p.krot, base + p.vt, k_rot_out, B, L, p.Lp, Hkv, D, 1, c - w,
                      dtype, st);
   if (e != hipSuccess) return DCA_ERR_HIP;
   if (dtype == DCA_F32) {
@@ -154,6 +184,10 @@ static int attend_impl(const void* q, void* o, float* lse, int64_t B, int64_t L,
   a.c = c;
   a.w = w;
   a.s = c - w;
+  a.map = kMapDCA;
+  a.krot2 = nullptr;
+  a.se_group = 1;
+  a.se_window = 0;
   a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
   return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }
@@ -206,6 +240,64 @@ int dca_prefill(const void* q, const void* k, const void* v, void* o, float* lse
   const int rp = prepare_impl(k, v, k_rot_out, B, L, Hkv, D, c, w, rope_base, dtype, ws, p, st);
   if (rp != DCA_OK) return rp;
   return attend_impl(q, o, lse, B, L, Hq, Hkv, D, c, w, sm_scale, dtype, ws, p, st);
+}
+
+size_t dca_selfextend_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int group,
+                                      int window, int dtype) {
+  SeLayout p;
+  return se_layout(B, L, Hkv, D, group, window, dtype, &p) ? p.total : 0;
+}
+
+int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int group,
+                           int window, double rope_base, float sm_scale, int dtype, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16) || !base_ok(rope_base) ||
+      !attend_args_ok(q, o, lse, B, L, Hq, Hkv, sm_scale))
+    return DCA_ERR_INVALID_ARG;
+  if (B < 1 || L < 1 || !se_ok(group, window)) return DCA_ERR_INVALID_ARG;
+  SeLayout p;
+  if (!se_layout(B, L, Hkv, D, group, window, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  double2* table = (double2*)(base + p.table);
+  if (launch_rope_table(table, (int)p.npos, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  // neighbor keys at j (with the V layout), grouped keys at floor(j / G)
+  const int unbounded = 1 << 30;
+  if (launch_kv_prep(k, v, table, base + p.krot, base + p.vt, nullptr, B, L, p.Lp, Hkv, D, 1, unbounded,
+                     dtype, st) != hipSuccess)
+    return DCA_ERR_HIP;
+  if (launch_kv_prep(k, v, table, base + p.krot2, nullptr, nullptr, B, L, p.Lp, Hkv, D, group, unbounded,
+                     dtype, st) != hipSuccess)
+    return DCA_ERR_HIP;
+  if (dtype == DCA_F32 &&
+      hipMemcpyAsync(base + p.vt, v, (size_t)(B * L * Hkv * D * 4), hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return DCA_ERR_HIP;
+  PrefillArgs a;
+  a.q = q;
+  a.krot = base + p.krot;
+  a.krot2 = base + p.krot2;
+  a.vt = base + p.vt;
+  a.table = table;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.L = (int)L;
+  a.Lp = (int)p.Lp;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.D = (int)D;
+  // DCA fields unused: one chunk as long as any sequence
+  a.c = unbounded;
+  a.w = 0;
+  a.s = unbounded;
+  a.map = kMapSelfExtend;
+  a.se_group = group;
+  a.se_window = window;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+  return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }
 
 size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,

@@ -22,6 +22,12 @@ __host__ __device__ inline int query_pos(int cls, int r, int s, int c) {
   return c - 1;
 }
 
+// SelfExtend ("LLM Maybe LongLM", abstract: grouped attention for distant
+// tokens, neighbor attention inside a window W).  Neighbor pairs (i - j < W)
+// keep positions i and j; grouped pairs put key j at floor(j / G) and query i
+// at floor(i / G) + W - floor(W / G), so their distance is at least W.
+__host__ __device__ inline int se_query_pos_grouped(int i, int G, int W) { return i / G + W - W / G; }
+
 // ---- bf16 <-> fp32 -----------------------------------------------------------
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 

@@ -11,29 +11,44 @@ constexpr int kPrefillTileKeys = 64;  // key rows per prefill K/V tile
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// RoPE cos/sin table [c][D/2] of double2 (cos, sin), all in fp64.
-hipError_t launch_rope_table(double2* table, int c, int D, double base, hipStream_t st);
+// RoPE cos/sin table [npos][D/2] of double2 (cos, sin), all in fp64.
+hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipStream_t st);
 
 // dca_rope_remap kernel (dtype 0 = fp32, 1 = bf16).
 hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
                              int64_t pos0, int map, int c, int w, double base, int dtype,
                              hipStream_t st);
 
-// Key rotation at j mod s into head-major krot [B, Hkv, Lp, D] (+ optional
-// BSHD copy), and for bf16 the tiled, key-permuted V transpose
+// Key rotation into head-major krot [B, Hkv, Lp, D] (+ optional BSHD copy):
+// key j is turned to position (j / kdiv) mod kmod (DCA: kdiv 1, kmod s;
+// SelfExtend neighbor keys: kdiv 1, grouped keys: kdiv G, kmod unbounded).
+// For bf16 with vt non-null, also the tiled, key-permuted V transpose
 // vt [B, Hkv, Lp/64, D, 64].
 hipError_t launch_kv_prep(const void* k, const void* v, const double2* table, void* krot, void* vt,
                           void* k_rot_out, int64_t B, int64_t L, int64_t Lp, int64_t Hkv, int64_t D,
-                          int s, int dtype, hipStream_t st);
+                          int kdiv, int kmod, int dtype, hipStream_t st);
+
+// Position maps of the prefill kernels.
+enum PosMap : int {
+  kMapDCA = 0,         // chunk relation: intra / successive / inter queries, keys at j mod s
+  kMapSelfExtend = 1,  // neighbor (i - j < W): plain positions; grouped: keys j/G,
+                       // queries i/G + W - W/G
+};
+// SelfExtend pair classes (the order the kernels visit them in).
+constexpr int kSeGrouped = 0;
+constexpr int kSeNeighbor = 1;
 
 struct PrefillArgs {
   const void* q;       // [B, L, Hq, D] raw
-  const void* krot;    // [B, Hkv, Lp, D] rotated keys
+  const void* krot;    // [B, Hkv, Lp, D] rotated keys (DCA: at j mod s; SelfExtend: at j)
+  const void* krot2;   // SelfExtend only: keys at floor(j / G); null for DCA
   const void* vt;      // bf16: [B, Hkv, Lp/64, D, 64]; fp32: raw v [B, L, Hkv, D]
-  const double2* table; // [c, D/2] (cos, sin) in fp64
+  const double2* table; // [npos, D/2] (cos, sin) in fp64
   void* o;             // [B, L, Hq, D]
   float* lse;          // [B, Hq, L] or null
   int B, L, Lp, Hq, Hkv, D, c, w, s;
+  int map;             // PosMap
+  int se_group, se_window;  // SelfExtend G and W
   float sm_scale;
 };
 

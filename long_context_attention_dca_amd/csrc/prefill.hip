@@ -377,7 +377,7 @@ constexpr int kBufferWord3 = 0x00020000;
 // data is only needed two phases later.
 __device__ inline void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D>
+template <int D, int MAP>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   constexpr int NDS = D / 16;
@@ -420,14 +420,42 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const int rq = qrow - nq * s;
   const int nkt = min(i0 + PP_BR - 1, L - 1) / BC + 1;
 
+  // ---- order in which key tiles are visited ("virtual tiles" t) -------------
+  // DCA: key tiles 0 .. nkt-1; a (wave, tile) pair has one chunk relation.
+  // SelfExtend: first the tiles holding grouped pairs of this workgroup's rows
+  // (j <= i - W), then those holding neighbor pairs (i - W < j <= i).  Tiles on
+  // the window edge are visited twice, each time with the other class masked;
+  // the class is the same for the whole workgroup, and selects the key
+  // rotation staged and the query variant used.
+  int n_gr = 0, nb_begin = 0, nvt = nkt;
+  if constexpr (MAP == kMapSelfExtend) {
+    const int W = a.se_window;
+    const int i_top = min(i0 + PP_BR - 1, L - 1);
+    n_gr = i_top >= W ? (i_top - W) / BC + 1 : 0;
+    nb_begin = max(i0 - W + 1, 0) / BC;
+    nvt = n_gr + (W > 0 ? nkt - nb_begin : 0);
+  }
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
+    if constexpr (MAP == kMapSelfExtend) return t < n_gr ? t : nb_begin + (t - n_gr);
+    return t;
+  };
+  auto class_of = [&](int t) __attribute__((always_inline)) {
+    if constexpr (MAP == kMapSelfExtend) return t < n_gr ? kSeGrouped : kSeNeighbor;
+    return min(nq - (t * BC) / s, 2);
+  };
+
   const uint16_t* qsrc = (const uint16_t*)a.q + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
   const uint16_t* kbase = (const uint16_t*)a.krot + bg * (int64_t)a.Lp * D;
   const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
 
   bf16x8 qf[NDS];
   auto load_q = [&](int cls) {
-    const int P = query_pos(cls, rq, s, c);
-    const double2* tb = a.table + (int64_t)P * (D / 2);
+    int P;
+    if constexpr (MAP == kMapSelfExtend)
+      P = cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window);
+    else
+      P = query_pos(cls, rq, s, c);
+    const double2* tb = a.table + (int64_t)P * (D / 2);   // read only for rows < L
     if (qrow < L) {
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds) {
@@ -474,18 +502,25 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const uint32_t head_bytes = (uint32_t)((int64_t)a.Lp * D * 2);
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, kBufferWord3);
-  auto issue_k = [&](int kt) {
-    const int soff = kt * BC * D * 2;
-    uint8_t* dst = smem + KB0 + (kt & 1) * Smem<D>::KBYTES;
+  __amdgpu_buffer_rsrc_t krsrc2 = krsrc;   // SelfExtend: grouped keys (at floor(j / G))
+  if constexpr (MAP == kMapSelfExtend)
+    krsrc2 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)a.krot2 + bg * (int64_t)a.Lp * D), (short)0, head_bytes, kBufferWord3);
+  auto issue_k = [&](int t) {
+    const int soff = tile_of(t) * BC * D * 2;
+    uint8_t* dst = smem + KB0 + (t & 1) * Smem<D>::KBYTES;
+    __amdgpu_buffer_rsrc_t rs = krsrc;
+    if constexpr (MAP == kMapSelfExtend)
+      if (class_of(t) == kSeGrouped) rs = krsrc2;
 #pragma unroll
     for (int i = 0; i < KPW; ++i)
       if (wave + 8 * i < Smem<D>::KPIECES)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
                                                  16, (int)koff[i], soff, 0, 0);
   };
-  auto issue_v = [&](int kt) {
-    const int soff = kt * BC * D * 2;
-    uint8_t* dst = smem + VB0 + (kt & 1) * Smem<D>::VBYTES;
+  auto issue_v = [&](int t) {
+    const int soff = tile_of(t) * BC * D * 2;
+    uint8_t* dst = smem + VB0 + (t & 1) * Smem<D>::VBYTES;
 #pragma unroll
     for (int i = 0; i < VPW; ++i)
       if (wave + 8 * i < Smem<D>::VPIECES)
@@ -528,15 +563,30 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
       }
   };
   auto do_softmax = [&](int t) {
-    const int j0 = t * BC;
-    if (j0 + BC - 1 > i_lo) {   // tile reaches past the wave's first row: causal mask
+    const int j0 = tile_of(t) * BC;
+    // Keys this lane keeps: [lo, hi].  DCA: the causal prefix.  SelfExtend:
+    // grouped j <= i - W, neighbor i - W < j <= i.  The mask is applied only
+    // when the tile is not wholly inside every row's range.
+    int lo = 0, hi = qrow;
+    bool need = j0 + BC - 1 > i_lo;
+    if constexpr (MAP == kMapSelfExtend) {
+      const int W = a.se_window;
+      if (class_of(t) == kSeGrouped) {
+        hi = qrow - W;
+        need = j0 + BC - 1 > i_lo - W;
+      } else {
+        lo = qrow - W + 1;
+        need = need || j0 < i_lo + 32 - W;
+      }
+    }
+    if (need) {
       const int jb = j0 + hh * 4;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = jb + kb2 * 32 + (v >> 2) * 8 + (v & 3);
-          sacc[kb2][v] = (j <= qrow) ? sacc[kb2][v] : -INFINITY;
+          sacc[kb2][v] = (j >= lo && j <= hi) ? sacc[kb2][v] : -INFINITY;
         }
     }
     // Probabilities against the running max first.  A lane whose 32
@@ -588,13 +638,13 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // so every iteration is straight-line code.  Tiles past a wave's last row
   // are processed fully masked (p = 0) rather than skipped.
   auto prep_q = [&](int t) {
-    const int cls = min(nq - (t * BC) / s, 2);
+    const int cls = class_of(t);
     if (cls != cur_cls) {
       load_q(cls);
       cur_cls = cls;
     }
   };
-  // X(t) for 0 < t < nkt: PV(t-1) then QK(t) as one chain of 32 MFMAs whose
+  // X(t) for 0 < t < nvt: PV(t-1) then QK(t) as one chain of 32 MFMAs whose
   // LDS operands are read NPRE fragments ahead (a ring of registers), so each
   // MFMA waits only for the oldest read in flight.
   auto x_full = [&](int t) {
@@ -639,8 +689,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   issue_k(0);
   wait_vmem();
   phase_barrier();
-  // tile 0 (the first X phase has no PV; the last one, at t = nkt, has no QK)
-  if (nkt > 1) issue_k(1);
+  // tile 0 (the first X phase has no PV; the last one, at t = nvt, has no QK)
+  if (nvt > 1) issue_k(1);
   issue_v(0);
   if (grp == 0) {
     prep_q(0);
@@ -649,8 +699,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     do_softmax(0);
     wait_vmem();
     phase_barrier();
-    for (int t = 1; t < nkt; ++t) {
-      if (t + 1 < nkt) issue_k(t + 1);
+    for (int t = 1; t < nvt; ++t) {
+      if (t + 1 < nvt) issue_k(t + 1);
       issue_v(t);
       x_full(t);
       phase_barrier();
@@ -658,7 +708,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
       wait_vmem();
       phase_barrier();
     }
-    do_pv(nkt - 1);
+    do_pv(nvt - 1);
     phase_barrier();
     phase_barrier();
   } else {
@@ -667,8 +717,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     do_qk(0);
     wait_vmem();
     phase_barrier();
-    for (int t = 1; t < nkt; ++t) {
-      if (t + 1 < nkt) issue_k(t + 1);
+    for (int t = 1; t < nvt; ++t) {
+      if (t + 1 < nvt) issue_k(t + 1);
       issue_v(t);
       do_softmax(t - 1);
       pin_p();
@@ -677,9 +727,9 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
       wait_vmem();
       phase_barrier();
     }
-    do_softmax(nkt - 1);
+    do_softmax(nvt - 1);
     phase_barrier();
-    do_pv(nkt - 1);
+    do_pv(nvt - 1);
     phase_barrier();
   }
 
@@ -703,14 +753,18 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 
 // ---- fp32 kernel (VALU, exact-arithmetic path for fp32 inputs) ---------------------
 // One workgroup = 16 query rows of one head; 16 lanes per row, 32-key tiles.
+// Every pair picks its query variant (and, for SelfExtend, its key rotation)
+// on its own.
 constexpr int FBR = 16, FBC = 32;
 
-template <int D>
+template <int D, int MAP>
 __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
   constexpr int HALF = D / 2;
   constexpr int NO = D / 16;
-  __shared__ float qv[3][D][FBR];
+  constexpr int NV = MAP == kMapSelfExtend ? 2 : 3;   // query variants
+  __shared__ float qv[NV][D][FBR];
   __shared__ float ks[FBC][D + 1];
+  __shared__ float ks2[MAP == kMapSelfExtend ? FBC : 1][D + 1];   // SelfExtend grouped keys
   __shared__ float vs[FBC][D];
   __shared__ float ps[FBR][FBC + 1];
   const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -722,21 +776,29 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
   const int i0 = qt * FBR, i = i0 + r;
   const float* q = (const float*)a.q;
   const float* krot = (const float*)a.krot + bg * (int64_t)a.Lp * D;
+  const float* krot2 = (const float*)a.krot2 + bg * (int64_t)a.Lp * D;   // SelfExtend only
   const float* vraw = (const float*)a.vt;
+  const int W = a.se_window;
 
   for (int idx = tid; idx < FBR * HALF; idx += 256) {
     const int rr = idx / HALF, k = idx - rr * HALF;
     const int ii = i0 + rr;
-    float x1 = 0.f, x2 = 0.f;
-    if (ii < L) {
-      const float* src = q + (((int64_t)b * L + ii) * a.Hq + hq) * D;
-      x1 = src[k];
-      x2 = src[k + HALF];
+    if (ii >= L) {   // padding rows: zero queries (their table position may not exist)
+#pragma unroll
+      for (int cls = 0; cls < NV; ++cls) qv[cls][k][rr] = qv[cls][k + HALF][rr] = 0.f;
+      continue;
     }
+    const float* src = q + (((int64_t)b * L + ii) * a.Hq + hq) * D;
+    const float x1 = src[k], x2 = src[k + HALF];
     const int rqq = ii % s;
 #pragma unroll
-    for (int cls = 0; cls < 3; ++cls) {
-      const double2 t = a.table[(int64_t)query_pos(cls, rqq, s, c) * HALF + k];
+    for (int cls = 0; cls < NV; ++cls) {
+      int P;
+      if constexpr (MAP == kMapSelfExtend)
+        P = cls == kSeNeighbor ? ii : se_query_pos_grouped(ii, a.se_group, W);
+      else
+        P = query_pos(cls, rqq, s, c);
+      const double2 t = a.table[(int64_t)P * HALF + k];
       qv[cls][k][rr] = (float)((double)x1 * t.x - (double)x2 * t.y);
       qv[cls][k + HALF][rr] = (float)((double)x2 * t.x + (double)x1 * t.y);
     }
@@ -754,6 +816,7 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
       const int row = idx / D, d = idx - row * D;
       const int j = j0 + row;
       ks[row][d] = krot[(int64_t)j * D + d];
+      if constexpr (MAP == kMapSelfExtend) ks2[row][d] = krot2[(int64_t)j * D + d];
       vs[row][d] = (j < L) ? vraw[(((int64_t)b * L + j) * a.Hkv + g) * D + d] : 0.f;
     }
     __syncthreads();
@@ -764,10 +827,18 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
       if (j > i || j >= L) {
         sc[e] = -INFINITY;
       } else {
-        const int cls = min(nq - j / s, 2);
         float acc = 0.f;
+        if constexpr (MAP == kMapSelfExtend) {
+          const bool grouped = i - j >= W;
+          const int cls = grouped ? kSeGrouped : kSeNeighbor;
+          const float* kr = grouped ? ks2[key] : ks[key];
 #pragma unroll 8
-        for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], ks[key][d], acc);
+          for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], kr[d], acc);
+        } else {
+          const int cls = min(nq - j / s, 2);
+#pragma unroll 8
+          for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], ks[key][d], acc);
+        }
         sc[e] = acc * a.sm_scale;
       }
     }
@@ -809,14 +880,22 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   const int xcd_map = ((int64_t)a.B * a.Hkv) % 8 == 0 ? 1 : 0;
   const float scale_log2 = a.sm_scale * kLog2e;
-  if (a.s % BC == 0) {
-    // every wave block and key tile lies inside one chunk: ping-pong kernel
+  if (a.map == kMapSelfExtend || a.s % BC == 0) {
+    // SelfExtend, or DCA with every wave block and key tile inside one chunk:
+    // ping-pong kernel
     const int nqt = (a.L + PP_BR - 1) / PP_BR;
     const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
-    if (a.D == 64)
-      hipLaunchKernelGGL(prefill_bf16_pp_kernel<64>, grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
-    else
-      hipLaunchKernelGGL(prefill_bf16_pp_kernel<128>, grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+    if (a.map == kMapSelfExtend) {
+      if (a.D == 64)
+        hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapSelfExtend>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+      else
+        hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapSelfExtend>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+    } else {
+      if (a.D == 64)
+        hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapDCA>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+      else
+        hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapDCA>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+    }
     return hipGetLastError();
   }
   const int nqt = (a.L + BR - 1) / BR;
@@ -830,10 +909,17 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.L + FBR - 1) / FBR), (unsigned)a.Hq, (unsigned)a.B);
-  if (a.D == 64)
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(256), 0, st, a);
+  if (a.map == kMapSelfExtend) {
+    if (a.D == 64)
+      hipLaunchKernelGGL((prefill_f32_kernel<64, kMapSelfExtend>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_f32_kernel<128, kMapSelfExtend>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.D == 64)
+      hipLaunchKernelGGL((prefill_f32_kernel<64, kMapDCA>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_f32_kernel<128, kMapDCA>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -4,16 +4,18 @@
 // "The Problem"): the pair (x_k, x_{k+D/2}) is turned by position * theta_k,
 // theta_k = base^(-2k/D).  DCA positions ("The Architecture" box and the
 // intra / inter / successive sections): keys at j mod s, queries at one of
-// three positions chosen by the chunk relation.
+// three positions chosen by the chunk relation.  SelfExtend ("LLM Maybe
+// LongLM", abstract) positions: neighbor pairs plain, grouped pairs with keys
+// at floor(j / G) and queries at floor(i / G) + W - floor(W / G).
 #include "dca_common.hpp"
 #include "dca_launch.hpp"
 
 namespace dca {
 
-// ---- cos/sin table [c][D/2] (fp64) -------------------------------------------------
-__global__ void rope_table_kernel(double2* __restrict__ table, int c, int half, int D, double base) {
+// ---- cos/sin table [npos][D/2] (fp64) ----------------------------------------------
+__global__ void rope_table_kernel(double2* __restrict__ table, int npos, int half, int D, double base) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= c * half) return;
+  if (idx >= npos * half) return;
   const int p = idx / half, k = idx - p * half;
   const double theta = pow(base, -2.0 * (double)k / (double)D);
   double sn, cs;
@@ -21,10 +23,10 @@ __global__ void rope_table_kernel(double2* __restrict__ table, int c, int half, 
   table[idx] = make_double2(cs, sn);
 }
 
-hipError_t launch_rope_table(double2* table, int c, int D, double base, hipStream_t st) {
+hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipStream_t st) {
   const int half = D / 2;
-  const int n = c * half;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, c, half, D,
+  const int n = npos * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, npos, half, D,
                      base);
   return hipGetLastError();
 }
@@ -32,9 +34,15 @@ hipError_t launch_rope_table(double2* table, int c, int D, double base, hipStrea
 // ---- dca_rope_remap -----------------------------------------------------------------
 // One workgroup per token t: the 64 (or 32) angles of its position are made
 // once in fp64 and applied to every (batch, head) row of that token.
+// Maps 0-4 take the DCA (c, w); the SelfExtend maps 5 and 6 take c = G and
+// w = W.
 __device__ inline int64_t remap_position(int64_t p, int map, int c, int w) {
   const int64_t s = c - w;
   switch (map) {
+    case 5:  // SelfExtend grouped key
+      return p / c;
+    case 6:  // SelfExtend grouped query
+      return p / c + w - w / c;
     case 0:  // key
     case 1:  // query, intra
       return p % s;
@@ -105,7 +113,7 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, c
                                                       const double2* __restrict__ table,
                                                       T* __restrict__ krot, uint16_t* __restrict__ vt,
                                                       T* __restrict__ k_rot_out, int L, int Lp, int Hkv,
-                                                      int s) {
+                                                      int kdiv, int kmod) {
   constexpr int half = D / 2;
   constexpr int TK = kPrefillTileKeys;
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -119,7 +127,7 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, c
       const int64_t in = (((int64_t)b * L + j) * Hkv + g) * D;
       const double x1 = Elem<T>::load(k + in + kk);
       const double x2 = Elem<T>::load(k + in + kk + half);
-      const double2 a = table[(j % s) * half + kk];
+      const double2 a = table[((j / kdiv) % kmod) * half + kk];
       const float y1 = (float)(x1 * a.x - x2 * a.y);
       const float y2 = (float)(x2 * a.x + x1 * a.y);
       Elem<T>::store(dst + kk, y1);
@@ -134,6 +142,7 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, c
     }
   }
   if constexpr (TRANSPOSE_V) {
+    if (vt == nullptr) return;   // uniform: a second key rotation without V
     __shared__ uint16_t vs[TK][D + 2];
     const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
     for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
@@ -154,25 +163,26 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, c
 template <typename T, bool TV>
 static void launch_prep_t(int D, dim3 grid, hipStream_t st, const void* k, const void* v,
                           const double2* table, void* krot, void* vt, void* k_rot_out, int L, int Lp,
-                          int Hkv, int s) {
+                          int Hkv, int kdiv, int kmod) {
   if (D == 64)
     hipLaunchKernelGGL((kv_prep_kernel<T, 64, TV>), grid, dim3(256), 0, st, (const T*)k, (const T*)v,
-                       table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, s);
+                       table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, kdiv, kmod);
   else
     hipLaunchKernelGGL((kv_prep_kernel<T, 128, TV>), grid, dim3(256), 0, st, (const T*)k,
-                       (const T*)v, table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, s);
+                       (const T*)v, table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, kdiv,
+                       kmod);
 }
 
 hipError_t launch_kv_prep(const void* k, const void* v, const double2* table, void* krot, void* vt,
                           void* k_rot_out, int64_t B, int64_t L, int64_t Lp, int64_t Hkv, int64_t D,
-                          int s, int dtype, hipStream_t st) {
+                          int kdiv, int kmod, int dtype, hipStream_t st) {
   const dim3 grid((unsigned)(Lp / kPrefillTileKeys), (unsigned)Hkv, (unsigned)B);
   if (dtype == 0)
     launch_prep_t<float, false>((int)D, grid, st, k, v, table, krot, vt, k_rot_out, (int)L, (int)Lp,
-                                (int)Hkv, s);
+                                (int)Hkv, kdiv, kmod);
   else
     launch_prep_t<uint16_t, true>((int)D, grid, st, k, v, table, krot, vt, k_rot_out, (int)L,
-                                  (int)Lp, (int)Hkv, s);
+                                  (int)Lp, (int)Hkv, kdiv, kmod);
   return hipGetLastError();
 }
 

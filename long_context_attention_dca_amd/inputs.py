@@ -69,4 +69,9 @@ WORKLOADS = {
                         c=4096, w=1024, base=10000.0, seed=3),
     "llama2_70b_128k": dict(kind="prefill", dtype="bf16", B=1, L=131072, Hq=64, Hkv=8, D=128,
                             c=4096, w=1024, base=10000.0, seed=4),
+    # SelfExtend grouped / neighbor attention on the 70B 32k shape.  The group
+    # size and neighbor window are not given by the pages: G = 8 and W = 1024
+    # (the same local window as the DCA workloads).
+    "selfextend_70b_32k": dict(kind="selfextend", dtype="bf16", B=1, L=32768, Hq=64, Hkv=8, D=128,
+                               group=8, window=1024, base=10000.0, seed=5),
 }

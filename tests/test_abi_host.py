@@ -131,7 +131,7 @@ def test_decode_rejects_before_touching_device(lib, over, status):
 @pytest.mark.parametrize("args,status", [
     ((None, FAKE, 1, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
     ((FAKE, FAKE, 1, 8, 2, 80, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_UNSUPPORTED),
-    ((FAKE, FAKE, 1, 8, 2, 64, 0, 5, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
+    ((FAKE, FAKE, 1, 8, 2, 64, 0, 9, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
     ((FAKE, FAKE, 1, 8, 2, 64, -1, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
     ((FAKE, FAKE, 1, 8, 2, 64, 0, 0, 128, 128, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
     ((FAKE, FAKE + 2, 1, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
@@ -161,3 +161,55 @@ def test_two_phase_prefill_validation(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_selfextend_workspace_sizes(lib):
+    # bf16, B 2, L 100, Hkv 3, D 128, G 4, W 16: positions up to max(99, 99//4 + 16 - 4) = 99
+    Lp = 128
+    table = 100 * 64 * 16
+    kbytes = 2 * 3 * Lp * 128 * 2
+    want = table + 3 * kbytes          # (each piece is already a multiple of 256)
+    assert lib.dca_selfextend_workspace_bytes(2, 100, 3, 128, 4, 16, 1) == want
+    # a wide window pushes the grouped query position past L - 1: 99//4 + 300 - 75 = 249
+    assert lib.dca_selfextend_workspace_bytes(2, 100, 3, 128, 4, 300, 1) == 250 * 64 * 16 + 3 * kbytes
+    assert lib.dca_selfextend_workspace_bytes(1, 100, 1, 128, 0, 16, 1) == 0    # group < 1
+    assert lib.dca_selfextend_workspace_bytes(1, 100, 1, 128, 4, -1, 1) == 0    # window < 0
+    assert lib.dca_selfextend_workspace_bytes(1, 100, 1, 96, 4, 16, 1) == 0     # head dim
+
+
+SE_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, L=256, Hq=4, Hkv=2, D=128, G=4, W=32,
+             base=10000.0, sm_scale=0.0, dtype=1, ws=FAKE_WS, ws_bytes=1 << 30, stream=None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(k=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(G=0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(W=-3), _lib.DCA_ERR_INVALID_ARG),
+    (dict(Hq=3), _lib.DCA_ERR_INVALID_ARG),
+    (dict(L=0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(D=80), _lib.DCA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.DCA_ERR_UNSUPPORTED),
+    (dict(lse=FAKE + 1), _lib.DCA_ERR_INVALID_ARG),
+    (dict(base=-1.0), _lib.DCA_ERR_INVALID_ARG),
+    (dict(ws_bytes=4096), _lib.DCA_ERR_WORKSPACE),
+    (dict(ws=None), _lib.DCA_ERR_WORKSPACE),
+])
+def test_selfextend_rejects_before_touching_device(lib, over, status):
+    a = dict(SE_OK, **over)
+    assert lib.dca_selfextend_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["L"], a["Hq"],
+                                      a["Hkv"], a["D"], a["G"], a["W"], a["base"], a["sm_scale"],
+                                      a["dtype"], a["ws"], a["ws_bytes"], a["stream"]) == status
+
+
+@pytest.mark.parametrize("map_,c,w,status", [
+    (_lib.DCA_MAP_SE_KEY_GROUPED, 4, 100, _lib.DCA_OK),      # w >= c is fine for the grouped maps
+    (_lib.DCA_MAP_SE_Q_GROUPED, 1, 0, _lib.DCA_OK),
+    (_lib.DCA_MAP_SE_KEY_GROUPED, 0, 8, _lib.DCA_ERR_INVALID_ARG),
+    (_lib.DCA_MAP_SE_Q_GROUPED, 4, -1, _lib.DCA_ERR_INVALID_ARG),
+    (7, 4, 8, _lib.DCA_ERR_INVALID_ARG),
+    (_lib.DCA_MAP_KEY, 4, 8, _lib.DCA_ERR_INVALID_ARG),         # DCA maps still need w < c
+])
+def test_remap_selfextend_map_validation(lib, map_, c, w, status):
+    # B = 0: a valid call is an empty no-op, so nothing reaches the device
+    assert lib.dca_rope_remap(FAKE, FAKE, 0, 8, 2, 64, 0, map_, c, w, 1e4, 1, None) == status
