@@ -75,7 +75,7 @@ def measured_traffic(key):
 
 def prefill_kernel_name(c, w, D):
     """The attention kernel the library launches for bf16 (chunk size s = c - w)."""
-    return f"prefill_bf16_pp_kernel<{D}>" if (c - w) % 64 == 0 else f"prefill_bf16_kernel<{D}>"
+    return f"prefill_bf16_pp_kernel<{D}, 0>" if (c - w) % 64 == 0 else f"prefill_bf16_kernel<{D}>"
 
 
 def cpu_baseline(q, k, v, cfg, seconds):
