@@ -17,6 +17,7 @@ from .dca_ref import (  # noqa: F401
     dca_prefill_ref,
     dca_prefill_formB,
     dca_decode_ref,
+    dca_prefill_chunk_ref,
     MAP_KEY,
     MAP_Q_INTRA,
     MAP_Q_SUCC,

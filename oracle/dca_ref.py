@@ -328,3 +328,61 @@ def dca_decode_ref(q, k_raw, v, c: int, w: int, base: float = 10000.0,
             O[bi, hi] = o[0]
             LSE[bi, hi] = lse[0]
     return O, LSE
+
+
+def dca_prefill_chunk_ref(q, k_raw, v, pos0, c: int, w: int, base: float = 10000.0,
+                          sm_scale: float | None = None, q_len=None, rows=None, heads=None):
+    """Chunked prefill over a KV prefix: the new tokens of one chunk per sequence.
+
+    q: [B, Lq, Hq, D] raw queries; row r of sequence b is the token at
+    absolute position pos0[b] + r.  k_raw, v: [B, Lk, Hkv, D] *unrotated* keys
+    and values of positions 0 .. Lk-1 (the prefix followed by the chunk).
+    pos0: int or per-sequence list; q_len: None (Lq rows each) or a
+    per-sequence count of valid rows (ragged chunks).  Returns O [B, rows,
+    heads, D] and LSE [B, heads, rows]; rows r >= q_len[b] give 0 and -inf.
+
+    Row r is row pos0[b] + r of the causal prefill definition: the relation of
+    each pair comes from absolute chunk indices, keys sit at j mod s, and keys
+    j > pos0[b] + r are masked.  (The DCA guide's "Strategic Recommendations"
+    pair DCA with serving that processes long prompts in pieces; a chunk must
+    produce exactly the rows the whole prompt would.)
+    """
+    q = _f64(q)
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k_raw.shape[1], k_raw.shape[2]
+    s = chunk_size(c, w)
+    scale = 1.0 / np.sqrt(D) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    p0 = np.broadcast_to(np.asarray(pos0, dtype=np.int64), (B,))
+    ql = np.full(B, Lq, dtype=np.int64) if q_len is None else np.asarray(q_len, dtype=np.int64)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = np.arange(Hq) if heads is None else np.asarray(heads, dtype=np.int64)
+    O = np.zeros((B, len(rows), len(heads), D))
+    LSE = np.full((B, len(heads), len(rows)), -np.inf)
+    kpos = key_position(np.arange(Lk), c, w)
+    for b in range(B):
+        if p0[b] + ql[b] > Lk:
+            raise ValueError("the cache must hold every key of the chunk")
+        cache = {}
+        for hi, h in enumerate(heads):
+            g = _kv_head(int(h), Hq, Hkv)
+            if g not in cache:
+                cache[g] = (rope_rotate(_f64(k_raw[b, :, g]), kpos, base), _f64(v[b, :, g]))
+            khat, vg = cache[g]
+            for ri, r in enumerate(rows):
+                r = int(r)
+                if r >= ql[b]:
+                    continue
+                i = int(p0[b]) + r
+                n = i // s
+                p_intra, p_succ, p_inter = query_positions(i, c, w)
+                S = np.empty(i + 1)
+                for lo, hi_, pq in ((n * s, i + 1, p_intra), ((n - 1) * s, n * s, p_succ),
+                                    (0, (n - 1) * s, p_inter)):
+                    lo = max(lo, 0)
+                    if hi_ <= lo:
+                        continue
+                    S[lo:hi_] = scale * (khat[lo:hi_] @ rope_rotate(q[b, r, h], pq, base))
+                o, lse = _softmax_rows(S[None, :], vg[: i + 1])
+                O[b, ri, hi] = o[0]
+                LSE[b, hi, ri] = lse[0]
+    return O, LSE

@@ -383,3 +383,45 @@ def test_pins_catch_wrong_pairing(monkeypatch):
     monkeypatch.setattr(oracle, "rope_rotate", interleaved)
     with pytest.raises(AssertionError):
         test_rope_closed_form_d4_pairing_and_frequencies()
+
+
+# ------------------------------------------------ chunked prefill (prefix) ---
+@pytest.mark.parametrize("pos0,Lq", [(0, 50), (37, 40), (64, 59), (100, 23)])
+def test_chunk_rows_equal_full_prefill_rows(pos0, Lq):
+    # Prefix consistency: the chunk's rows are rows pos0.. of the whole prompt.
+    c, w = 32, 8
+    L = pos0 + Lq
+    q, k, v = inputs.prefill_inputs(2, L, 4, 2, 16, "f32", seed=13, qk_scale=2.0)
+    O, LSE = oracle.dca_prefill_ref(q, k, v, c, w, 10000.0, rows=np.arange(pos0, L))
+    Oc, Lc = oracle.dca_prefill_chunk_ref(q[:, pos0:], k, v, pos0, c, w, 10000.0)
+    assert np.abs(Oc - O).max() < 1e-13
+    assert np.abs(Lc - LSE).max() < 1e-13
+
+
+def test_chunks_concatenate_to_the_full_prefill():
+    c, w = 24, 6
+    L = 130
+    q, k, v = inputs.prefill_inputs(1, L, 2, 1, 8, "f32", seed=14, qk_scale=2.0)
+    O, _ = oracle.dca_prefill_ref(q, k, v, c, w, 10000.0)
+    parts = [oracle.dca_prefill_chunk_ref(q[:, a:b], k[:, :b], v[:, :b], a, c, w, 10000.0)[0]
+             for a, b in ((0, 40), (40, 41), (41, 100), (100, 130))]
+    assert np.abs(np.concatenate(parts, axis=1) - O).max() < 1e-13
+
+
+def test_single_row_chunk_is_decode_and_ragged_rows_are_independent():
+    c, w = 32, 8
+    q, k, v = inputs.prefill_inputs(2, 90, 4, 2, 16, "f32", seed=15, qk_scale=2.0)
+    Od, Ld = oracle.dca_decode_ref(q[:, 89], k, v, c, w, 10000.0)
+    Oc, Lc = oracle.dca_prefill_chunk_ref(q[:, 89:90], k, v, 89, c, w, 10000.0)
+    assert np.abs(Oc[:, 0] - Od).max() < 1e-13 and np.abs(Lc[:, :, 0] - Ld).max() < 1e-13
+    # ragged: sequence 1 has its chunk at a different offset and fewer rows
+    pos0, q_len = [60, 45], [30, 12]
+    qc = torch.zeros(2, 30, 4, 16, dtype=torch.float32)
+    qc[0] = q[0, 60:90]
+    qc[1, :12] = q[1, 45:57]
+    Or, Lr = oracle.dca_prefill_chunk_ref(qc, k, v, pos0, c, w, 10000.0, q_len=q_len)
+    O0, _ = oracle.dca_prefill_ref(q[0:1], k[0:1], v[0:1], c, w, 10000.0, rows=np.arange(60, 90))
+    O1, _ = oracle.dca_prefill_ref(q[1:2], k[1:2], v[1:2], c, w, 10000.0, rows=np.arange(45, 57))
+    assert np.abs(Or[0] - O0[0]).max() < 1e-13
+    assert np.abs(Or[1, :12] - O1[0]).max() < 1e-13
+    assert np.all(Or[1, 12:] == 0) and np.all(np.isneginf(Lr[1, :, 12:]))
