@@ -159,6 +159,44 @@ int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L,
                        const void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dca_prefill_chunk - DCA causal prefill of one chunk of new tokens per
+ * sequence, over a KV cache that already holds the sequence's earlier tokens
+ * (chunked prefill; ragged batches).
+ *
+ * Definition: new token r of sequence b is row pos0[b] + r of the dca_prefill
+ * definition.  The chunk relation of every pair is taken from absolute
+ * positions, so a prompt processed chunk by chunk gives the rows of the whole
+ * prompt.  This is the serving side of the DCA guide's "Strategic
+ * Recommendations": long prompts are held in a large KV cache.
+ *
+ *   q        : [B, Lq, Hq, D] raw queries; row r of sequence b is the token at
+ *              position pos0[b] + r.
+ *   k_cache  : [B, cache_len, Hkv, D] keys rotated at j mod s for positions
+ *              0 .. pos0[b] + q_len[b] - 1.  The chunk's own keys must be in
+ *              it: write them first with dca_rope_remap(DCA_MAP_KEY, pos0[b]).
+ *              Later rows are not read.
+ *   v_cache  : [B, cache_len, Hkv, D] values of the same positions.
+ *   o        : [B, Lq, Hq, D]; lse : [B, Hq, Lq] fp32 or NULL.  Rows
+ *              r >= q_len[b] are left untouched.
+ *   pos0     : HOST array of B offsets, pos0[b] >= 0.
+ *   q_len    : HOST array of B row counts with 0 <= q_len[b] <= Lq, or NULL
+ *              for Lq each.  Also pos0[b] + q_len[b] <= cache_len and
+ *              Lq <= cache_len.
+ *   ws       : at least dca_prefill_workspace_bytes(B, max_b(pos0[b] + q_len[b]),
+ *              Hkv, D, c, dtype) bytes.
+ * The host arrays are read during the call only.  The used cache rows are
+ * copied into the tiled key / value layout of the workspace, then the prefill
+ * kernels run with a query offset per sequence.  The two-group kernel is used
+ * when s is a multiple of 64 and every pos0[b] a multiple of 32.  Larger
+ * batches are processed in groups of 64 sequences.
+ */
+int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int64_t* pos0, const int64_t* q_len, int64_t B, int64_t Lq,
+                      int64_t cache_len, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
+                      double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
  * SelfExtend-style grouped / neighbor attention through the same prefill
  * kernels.
  *
@@ -221,6 +259,25 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
                double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
                void* stream);
+
+/*
+ * dca_decode_varlen - dca_decode for a ragged batch: sequence b holds kv_len[b]
+ * cached tokens (its new token included) and its new token sits at position
+ * kv_len[b] - 1.
+ *
+ *   kv_len   : HOST array of B lengths, 1 <= kv_len[b] <= cache_len (read
+ *              during the call only).
+ *   k_cache, v_cache : [B, cache_len, Hkv, D]; rows >= kv_len[b] are not read.
+ *   ws       : at least dca_decode_workspace_bytes(B, max_b kv_len[b], Hq, Hkv,
+ *              D, dtype) bytes.
+ * Everything else as in dca_decode.  Key ranges past a sequence's end
+ * contribute nothing to the merge.  Larger batches are processed in groups
+ * of 64 sequences.
+ */
+int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
+                      int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
+                      size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,10 +14,16 @@ Entry points (same names as include/dca.h):
          return_lse=False, workspace=None)
   selfextend_prefill(q, k, v, group, window, base=1e4, sm_scale=None,
                      return_lse=False, workspace=None)
+  prefill_chunk(q, k_cache, v_cache, pos0, c, w, base=1e4, sm_scale=None,
+                q_len=None, return_lse=False, out=None, workspace=None)
+  decode_varlen(q, k_cache, v_cache, kv_len, c, w, base=1e4, sm_scale=None,
+                return_lse=False, workspace=None)
   prefill_workspace_bytes(...), decode_workspace_bytes(...),
   selfextend_workspace_bytes(...)
 """
 from __future__ import annotations
+
+import ctypes
 
 import torch
 
@@ -28,7 +34,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
-           "selfextend_prefill", "prefill_workspace_bytes", "decode_workspace_bytes",
+           "selfextend_prefill", "prefill_chunk", "decode_varlen", "prefill_workspace_bytes", "decode_workspace_bytes",
            "selfextend_workspace_bytes", "DCAError", "library_path"]
 
 _DT = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}
@@ -220,5 +226,80 @@ def selfextend_prefill(q, k, v, group: int, window: int, base: float = 10000.0,
     _lib.check("dca_selfextend_prefill", lib.dca_selfextend_prefill(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
         B, L, Hq, Hkv, D, group, window, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def _host_i64(values, n: int, name: str):
+    """A host int64 array of n entries for the C ABI (an int broadcasts)."""
+    if isinstance(values, int):
+        values = [values] * n
+    values = [int(x) for x in (values.tolist() if hasattr(values, "tolist") else values)]
+    if len(values) != n:
+        raise ValueError(f"{name} needs {n} entries, got {len(values)}")
+    return (ctypes.c_int64 * n)(*values), values
+
+
+def prefill_chunk(q, k_cache, v_cache, pos0, c: int, w: int, base: float = 10000.0,
+                  sm_scale: float | None = None, q_len=None, return_lse: bool = False, out=None,
+                  workspace=None):
+    """Chunked DCA prefill over a KV cache.  q [B, Lq, Hq, D] raw queries of the new
+    tokens (row r of sequence b at position pos0[b] + r); caches [B, cache_len, Hkv, D]
+    with keys already rotated at j mod s, the chunk's own keys included.  pos0 and
+    q_len: an int or one entry per sequence (q_len None: Lq rows each).  Rows past
+    q_len[b] of the output are left as they were (zeros when out is None)."""
+    lib = _lib.load()
+    _check(q, "q", 4)
+    _check(k_cache, "k_cache", 4, q.dtype)
+    _check(v_cache, "v_cache", 4, q.dtype)
+    B, Lq, Hq, D = q.shape
+    cache_len, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, cache_len, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    code = _dtype_code(q)
+    p0, p0v = _host_i64(pos0, B, "pos0")
+    if q_len is None:
+        ql, qlv = None, [Lq] * B
+    else:
+        ql, qlv = _host_i64(q_len, B, "q_len")
+    o = torch.zeros_like(q) if out is None else out
+    _check(o, "out", 4, q.dtype)
+    lse = torch.full((B, Hq, Lq), float("-inf"), dtype=torch.float32, device=q.device) if return_lse else None
+    max_keys = max(a + n for a, n in zip(p0v, qlv))
+    nbytes = int(lib.dca_prefill_workspace_bytes(B, max(max_keys, 1), Hkv, D, c, code))
+    if nbytes == 0:
+        raise ValueError("invalid chunked prefill sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_prefill_chunk", lib.dca_prefill_chunk(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), _ptr(lse), p0, ql,
+        B, Lq, cache_len, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def decode_varlen(q, k_cache, v_cache, kv_len, c: int, w: int, base: float = 10000.0,
+                  sm_scale: float | None = None, return_lse: bool = False, workspace=None):
+    """DCA decode of a ragged batch: sequence b holds kv_len[b] cached tokens (its new
+    token at kv_len[b] - 1).  q [B, Hq, D] raw; caches [B, cache_len, Hkv, D], keys
+    rotated at j mod s."""
+    lib = _lib.load()
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4, q.dtype)
+    _check(v_cache, "v_cache", 4, q.dtype)
+    B, Hq, D = q.shape
+    cache_len, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, cache_len, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    code = _dtype_code(q)
+    kl, klv = _host_i64(kv_len, B, "kv_len")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(lib.dca_decode_workspace_bytes(B, max(klv), Hq, Hkv, D, code))
+    if nbytes == 0:
+        raise ValueError("invalid decode sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_decode_varlen", lib.dca_decode_varlen(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), _ptr(lse), kl,
+        B, cache_len, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
         ws.data_ptr(), nbytes, _stream(q.device)))
     return (o, lse) if return_lse else o

@@ -26,6 +26,7 @@ DCA_ERR_HIP = -4
 _i64, _int, _dbl, _flt, _vp, _sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float,
                                     ctypes.c_void_p, ctypes.c_size_t)
 _fp = ctypes.POINTER(ctypes.c_float)
+_i64p = ctypes.POINTER(ctypes.c_int64)   # host int64 arrays
 
 # name -> (restype, argtypes); the exported surface of include/dca.h
 SIGNATURES = {
@@ -42,7 +43,11 @@ SIGNATURES = {
     "dca_selfextend_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _int]),
     "dca_selfextend_prefill": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int,
                                       _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_prefill_chunk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64, _i64,
+                                 _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "dca_decode_varlen": (_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _int, _int,
+                                 _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _dbl,
                           _flt, _int, _vp, _sz, _vp]),
 }

@@ -154,8 +154,22 @@ static int prepare_impl(const void* k, const void* v, void* k_rot_out, int64_t B
   double2* table = (double2*)(base + p.table);
   hipError_t e = launch_rope_table(table, c, (int)D, rope_base, st);
   if (e != hipSuccess) return DCA_ERR_HIP;
-  e = launch_kv_prep(k, v, table, base + p.krot, base + p.vt, k_rot_out, B, L, p.Lp, Hkv, D, 1, c - w,
-                     dtype, st);
+  KvPrepArgs kp = {};
+  kp.k = k;
+  kp.v = v;
+  kp.table = table;
+  kp.krot = base + p.krot;
+  kp.vt = base + p.vt;
+  kp.k_rot_out = k_rot_out;
+  kp.B = (int)B;
+  kp.in_rows = (int)L;
+  kp.L = (int)L;
+  kp.Lp = (int)p.Lp;
+  kp.Hkv = (int)Hkv;
+  kp.D = (int)D;
+  kp.kdiv = 1;
+  kp.kmod = c - w;
+  e = launch_kv_prep(kp, dtype, st);
   if (e != hipSuccess) return DCA_ERR_HIP;
   if (dtype == DCA_F32) {
     e = hipMemcpyAsync(base + p.vt, v, (size_t)(B * L * Hkv * D * 4), hipMemcpyDeviceToDevice, st);
@@ -168,7 +182,7 @@ static int attend_impl(const void* q, void* o, float* lse, int64_t B, int64_t L,
                        int64_t Hkv, int64_t D, int c, int w, float sm_scale, int dtype,
                        const void* ws, const PrefillLayout& p, hipStream_t st) {
   const uint8_t* base = (const uint8_t*)ws;
-  PrefillArgs a;
+  PrefillArgs a = {};
   a.q = q;
   a.krot = base + p.krot;
   a.vt = base + p.vt;
@@ -188,6 +202,9 @@ static int attend_impl(const void* q, void* o, float* lse, int64_t B, int64_t L,
   a.krot2 = nullptr;
   a.se_group = 1;
   a.se_window = 0;
+  a.q_rows = (int)L;
+  a.per_seq = 0;
+  a.v_rows = (int)L;
   a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
   return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }
@@ -266,16 +283,29 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   if (launch_rope_table(table, (int)p.npos, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
   // neighbor keys at j (with the V layout), grouped keys at floor(j / G)
   const int unbounded = 1 << 30;
-  if (launch_kv_prep(k, v, table, base + p.krot, base + p.vt, nullptr, B, L, p.Lp, Hkv, D, 1, unbounded,
-                     dtype, st) != hipSuccess)
-    return DCA_ERR_HIP;
-  if (launch_kv_prep(k, v, table, base + p.krot2, nullptr, nullptr, B, L, p.Lp, Hkv, D, group, unbounded,
-                     dtype, st) != hipSuccess)
-    return DCA_ERR_HIP;
+  KvPrepArgs kp = {};
+  kp.k = k;
+  kp.v = v;
+  kp.table = table;
+  kp.krot = base + p.krot;
+  kp.vt = base + p.vt;
+  kp.B = (int)B;
+  kp.in_rows = (int)L;
+  kp.L = (int)L;
+  kp.Lp = (int)p.Lp;
+  kp.Hkv = (int)Hkv;
+  kp.D = (int)D;
+  kp.kdiv = 1;
+  kp.kmod = unbounded;
+  if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
+  kp.krot = base + p.krot2;
+  kp.vt = nullptr;
+  kp.kdiv = group;
+  if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
   if (dtype == DCA_F32 &&
       hipMemcpyAsync(base + p.vt, v, (size_t)(B * L * Hkv * D * 4), hipMemcpyDeviceToDevice, st) != hipSuccess)
     return DCA_ERR_HIP;
-  PrefillArgs a;
+  PrefillArgs a = {};
   a.q = q;
   a.krot = base + p.krot;
   a.krot2 = base + p.krot2;
@@ -296,6 +326,9 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   a.map = kMapSelfExtend;
   a.se_group = group;
   a.se_window = window;
+  a.q_rows = (int)L;
+  a.per_seq = 0;
+  a.v_rows = (int)L;
   a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
   return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }
@@ -322,7 +355,7 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
-  DecodeArgs a;
+  DecodeArgs a = {};
   a.q = q;
   a.kc = k_cache;
   a.vc = v_cache;
@@ -343,7 +376,146 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
   a.keys_per_split = p.kps;
   a.nsplit = p.ns;
+  a.cache_len = (int)kv_len;
+  a.per_seq = 0;
   return hip_status(launch_decode(a, dtype, (hipStream_t)stream));
+}
+
+int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int64_t* pos0, const int64_t* q_len, int64_t B, int64_t Lq, int64_t cache_len,
+                      int64_t Hq, int64_t Hkv, int64_t D, int c, int w, double rope_base, float sm_scale,
+                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!k_cache || !v_cache || !pos0 || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !base_ok(rope_base) || !cw_ok(c, w) || !attend_args_ok(q, o, lse, B, Lq, Hq, Hkv, sm_scale))
+    return DCA_ERR_INVALID_ARG;
+  if (B < 1 || Lq < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || Lq > cache_len) return DCA_ERR_INVALID_ARG;
+  // per-sequence offsets and lengths (host memory, read here)
+  int64_t max_keys = 0, rows = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t n = q_len ? q_len[b] : Lq;
+    if (pos0[b] < 0 || n < 0 || n > Lq || pos0[b] + n > cache_len) return DCA_ERR_INVALID_ARG;
+    max_keys = pos0[b] + n > max_keys ? pos0[b] + n : max_keys;
+    rows += n;
+  }
+  if (rows == 0) return DCA_OK;   // no sequence has a row: nothing to do
+  PrefillLayout p;
+  if (!prefill_layout(B, max_keys, Hkv, D, c, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  double2* table = (double2*)(base + p.table);
+  if (launch_rope_table(table, c, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  const int64_t es = elem_size(dtype);
+  const int64_t kv_seq = cache_len * Hkv * D * es;    // bytes of one sequence's cache
+  const int64_t ws_seq = Hkv * p.Lp * D * es;         // bytes of one sequence's tiles
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxSeqGroup) {
+    const int nb = (int)(B - b0 < kMaxSeqGroup ? B - b0 : kMaxSeqGroup);
+    // copy the cached (already rotated) keys and the values into the tiles
+    KvPrepArgs kp = {};
+    kp.k = (const uint8_t*)k_cache + b0 * kv_seq;
+    kp.v = (const uint8_t*)v_cache + b0 * kv_seq;
+    kp.table = nullptr;
+    kp.krot = base + p.krot + b0 * ws_seq;
+    kp.vt = dtype == DCA_BF16 ? base + p.vt + b0 * ws_seq : nullptr;
+    kp.B = nb;
+    kp.in_rows = (int)cache_len;
+    kp.Lp = (int)p.Lp;
+    kp.Hkv = (int)Hkv;
+    kp.D = (int)D;
+    kp.kdiv = 1;
+    kp.kmod = 1 << 30;
+    kp.per_seq = 1;
+    PrefillArgs a = {};
+    for (int i = 0; i < nb; ++i) {
+      const int64_t n = q_len ? q_len[b0 + i] : Lq;
+      kp.seq_len[i] = (int)(pos0[b0 + i] + n);
+      a.seq_q0[i] = (int)pos0[b0 + i];
+      a.seq_len[i] = (int)n;
+    }
+    kp.L = (int)max_keys;
+    if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
+    a.q = (const uint8_t*)q + b0 * Lq * Hq * D * es;
+    a.krot = kp.krot;
+    a.krot2 = nullptr;
+    // bf16 reads the V tiles; fp32 reads the cache's values directly
+    a.vt = dtype == DCA_BF16 ? kp.vt : kp.v;
+    a.table = table;
+    a.o = (uint8_t*)o + b0 * Lq * Hq * D * es;
+    a.lse = lse ? lse + b0 * Hq * Lq : nullptr;
+    a.B = nb;
+    a.L = (int)max_keys;
+    a.Lp = (int)p.Lp;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.D = (int)D;
+    a.c = c;
+    a.w = w;
+    a.s = c - w;
+    a.map = kMapDCA;
+    a.se_group = 1;
+    a.q_rows = (int)Lq;
+    a.per_seq = 1;
+    a.v_rows = (int)cache_len;
+    a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+    const hipError_t e = dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st);
+    if (e != hipSuccess) return DCA_ERR_HIP;
+  }
+  return DCA_OK;
+}
+
+int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
+                      int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !o || !kv_len) return DCA_ERR_INVALID_ARG;
+  if (B < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || Hq < 1 || Hkv < 1 || Hq % Hkv)
+    return DCA_ERR_INVALID_ARG;
+  if (!cw_ok(c, w) || !base_ok(rope_base) || !isfinite(sm_scale)) return DCA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return DCA_ERR_INVALID_ARG;
+  int64_t max_kv = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    if (kv_len[b] < 1 || kv_len[b] > cache_len) return DCA_ERR_INVALID_ARG;
+    max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
+  }
+  DecodeLayout p;
+  if (!decode_layout(B, max_kv, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  const int64_t es = elem_size(dtype);
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxSeqGroup) {
+    const int nb = (int)(B - b0 < kMaxSeqGroup ? B - b0 : kMaxSeqGroup);
+    DecodeArgs a = {};
+    a.q = (const uint8_t*)q + b0 * Hq * D * es;
+    a.kc = (const uint8_t*)k_cache + b0 * cache_len * Hkv * D * es;
+    a.vc = (const uint8_t*)v_cache + b0 * cache_len * Hkv * D * es;
+    a.o = (uint8_t*)o + b0 * Hq * D * es;
+    a.lse = lse ? lse + b0 * Hq : nullptr;
+    a.qv = base + p.qv + b0 * Hq * 3 * D * es;
+    a.part_o = (float*)(base + p.part_o) + b0 * Hq * (int64_t)p.ns * D;
+    a.part_lse = (float*)(base + p.part_lse) + b0 * Hq * (int64_t)p.ns;
+    a.B = nb;
+    a.kv_len = (int)max_kv;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.D = (int)D;
+    a.c = c;
+    a.w = w;
+    a.s = c - w;
+    a.base = rope_base;
+    a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+    a.keys_per_split = p.kps;
+    a.nsplit = p.ns;
+    a.cache_len = (int)cache_len;
+    a.per_seq = 1;
+    for (int i = 0; i < nb; ++i) a.seq_len[i] = (int)kv_len[b0 + i];
+    const hipError_t e = launch_decode(a, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return DCA_ERR_HIP;
+  }
+  return DCA_OK;
 }
 
 }  // extern "C"

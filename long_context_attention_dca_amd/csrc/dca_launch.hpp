@@ -8,6 +8,9 @@
 namespace dca {
 
 constexpr int kPrefillTileKeys = 64;  // key rows per prefill K/V tile
+// Sequences whose own lengths / offsets one launch carries in its kernel
+// arguments (ragged batches are launched in groups of at most this many).
+constexpr int kMaxSeqGroup = 64;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -22,11 +25,22 @@ hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int
 // Key rotation into head-major krot [B, Hkv, Lp, D] (+ optional BSHD copy):
 // key j is turned to position (j / kdiv) mod kmod (DCA: kdiv 1, kmod s;
 // SelfExtend neighbor keys: kdiv 1, grouped keys: kdiv G, kmod unbounded).
-// For bf16 with vt non-null, also the tiled, key-permuted V transpose
-// vt [B, Hkv, Lp/64, D, 64].
-hipError_t launch_kv_prep(const void* k, const void* v, const double2* table, void* krot, void* vt,
-                          void* k_rot_out, int64_t B, int64_t L, int64_t Lp, int64_t Hkv, int64_t D,
-                          int kdiv, int kmod, int dtype, hipStream_t st);
+// With table == null the keys are already rotated (a KV cache) and are
+// copied as they are.  For bf16 with vt non-null, also the tiled,
+// key-permuted V transpose vt [B, Hkv, Lp/64, D, 64].  Rows at or past a
+// sequence's valid length are written as zeros.
+struct KvPrepArgs {
+  const void* k;        // [B, in_rows, Hkv, D]
+  const void* v;        // [B, in_rows, Hkv, D]
+  const double2* table; // rotation table, or null (copy)
+  void* krot;
+  void* vt;             // null: keys only
+  void* k_rot_out;      // [B, in_rows, Hkv, D] copy of the rotated keys, or null
+  int B, in_rows, L, Lp, Hkv, D, kdiv, kmod;
+  int per_seq;          // 1: seq_len[b] valid rows per sequence (else L)
+  int seq_len[kMaxSeqGroup];
+};
+hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st);
 
 // Position maps of the prefill kernels.
 enum PosMap : int {
@@ -50,6 +64,16 @@ struct PrefillArgs {
   int map;             // PosMap
   int se_group, se_window;  // SelfExtend G and W
   float sm_scale;
+  // Query rows.  Whole prompts (per_seq 0): query row r of every sequence is
+  // the token at position r, r < L, and q / o / lse hold q_rows = L rows.
+  // Chunks (per_seq 1): sequence b's query row r is the token at position
+  // seq_q0[b] + r for r < seq_len[b]; its keys are [0, seq_q0[b] + seq_len[b]);
+  // q / o / lse hold q_rows rows per sequence.  L is then the largest key count.
+  int q_rows;
+  int per_seq;
+  int seq_q0[kMaxSeqGroup];
+  int seq_len[kMaxSeqGroup];
+  int v_rows;          // fp32 kernels: rows per sequence of the raw V in vt
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
@@ -69,6 +93,12 @@ struct DecodeArgs {
   float sm_scale;
   int keys_per_split;  // multiple of 32
   int nsplit;          // NS
+  // Rows per sequence in the caches (the row stride; kv_len for a uniform
+  // batch).  per_seq 1: sequence b uses seq_len[b] cached keys and its new
+  // token sits at seq_len[b] - 1 (else every sequence uses kv_len).
+  int cache_len;
+  int per_seq;
+  int seq_len[kMaxSeqGroup];
 };
 
 // Split plan shared by the workspace query and the launcher.

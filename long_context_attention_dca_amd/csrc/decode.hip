@@ -45,15 +45,20 @@ __device__ inline int swz(int row, int chunk) {
 }
 
 // ---- 1. query variants -------------------------------------------------------------
+// The new token of sequence b sits at (its cached key count) - 1.
+__device__ inline int seq_keys(const DecodeArgs& a, int b) { return a.per_seq ? a.seq_len[b] : a.kv_len; }
+
 template <typename T>
-__global__ void decode_qprep_kernel(const T* __restrict__ q, T* __restrict__ qv, int D, int c, int s,
-                                    int qpos, double base) {
+__global__ void decode_qprep_kernel(DecodeArgs a) {
   const int bh = blockIdx.x, k = threadIdx.x;
+  const int D = a.D, c = a.c, s = a.s;
   const int half = D / 2;
   if (k >= half) return;
-  const T* src = q + (int64_t)bh * D;
+  const T* src = (const T*)a.q + (int64_t)bh * D;
+  T* qv = (T*)a.qv;
   const double x1 = Elem<T>::load(src + k), x2 = Elem<T>::load(src + k + half);
-  const double theta = pow(base, -2.0 * (double)k / (double)D);
+  const double theta = pow(a.base, -2.0 * (double)k / (double)D);
+  const int qpos = seq_keys(a, bh / a.Hq) - 1;
   const int r = qpos % s;
 #pragma unroll
   for (int cls = 0; cls < 3; ++cls) {
@@ -93,17 +98,17 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   const int qi = qg * 32 + ql;   // index inside the GQA group
   const bool qvalid = qi < G;
   const int hq = g * G + (qvalid ? qi : 0);
-  const int kv_len = a.kv_len, s = a.s;
+  const int kv_len = seq_keys(a, b), s = a.s;
   const int kbeg = split * a.keys_per_split;
-  const int kend = min(kbeg + a.keys_per_split, kv_len);
+  const int kend = min(kbeg + a.keys_per_split, kv_len);   // may be empty (ragged batch)
   const int qpos = kv_len - 1;
   const int nq = qpos / s;
 
   uint8_t* kl = smem + wave * WBYTES;
   uint8_t* vl = kl + KBYTES;
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive keys
-  const uint16_t* kc = (const uint16_t*)a.kc + ((int64_t)b * kv_len * a.Hkv + g) * D;
-  const uint16_t* vc = (const uint16_t*)a.vc + ((int64_t)b * kv_len * a.Hkv + g) * D;
+  const uint16_t* kc = (const uint16_t*)a.kc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
+  const uint16_t* vc = (const uint16_t*)a.vc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
   const uint16_t* qv = (const uint16_t*)a.qv + ((int64_t)b * a.Hq + hq) * 3 * D;
 
   bf16x8 qf[NDS];
@@ -268,7 +273,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   if (qvalid) {
     const int64_t pidx = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
     float* po = a.part_o + pidx * D;
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // empty range: O 0, LSE -inf
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -291,16 +296,16 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
   const int D = a.D;
   const int b = bh / a.Hq, hq = bh - b * a.Hq;
   const int G = a.Hq / a.Hkv, g = hq / G;
-  const int kv_len = a.kv_len, s = a.s;
+  const int kv_len = seq_keys(a, b), s = a.s;
   const int kbeg = split * a.keys_per_split;
-  const int kend = min(kbeg + a.keys_per_split, kv_len);
+  const int kend = min(kbeg + a.keys_per_split, kv_len);   // may be empty (ragged batch)
   const int nq = (kv_len - 1) / s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float* qv = (const float*)a.qv + (int64_t)bh * 3 * D;
   for (int idx = tid; idx < 3 * D; idx += 256) qs[idx / D][idx % D] = qv[idx];
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const float* kc = (const float*)a.kc + ((int64_t)b * kv_len * a.Hkv + g) * D;
-  const float* vc = (const float*)a.vc + ((int64_t)b * kv_len * a.Hkv + g) * D;
+  const float* kc = (const float*)a.kc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
+  const float* vc = (const float*)a.vc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
   float m = -INFINITY, l = 0.f, o = 0.f;  // thread tid < D owns output dim tid
   __syncthreads();
   for (int jb = kbeg; jb < kend; jb += 256) {
@@ -339,7 +344,7 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
   }
   if (tid < D) {
     const int64_t pidx = (int64_t)bh * a.nsplit + split;
-    a.part_o[pidx * D + tid] = o / l;
+    a.part_o[pidx * D + tid] = l > 0.f ? o / l : 0.f;   // empty range: O 0, LSE -inf
     if (tid == 0) a.part_lse[pidx] = (m + logf(l)) * kLog2e;
   }
 }
@@ -405,17 +410,14 @@ void decode_plan(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int dtype, 
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
-  const int qpos = a.kv_len - 1;
   const int nbh = a.B * a.Hq;
   if (dtype == 0) {
-    hipLaunchKernelGGL(decode_qprep_kernel<float>, dim3(nbh), dim3(64), 0, st, (const float*)a.q,
-                       (float*)a.qv, a.D, a.c, a.s, qpos, a.base);
+    hipLaunchKernelGGL(decode_qprep_kernel<float>, dim3(nbh), dim3(64), 0, st, a);
     hipLaunchKernelGGL(decode_split_f32_kernel, dim3(a.nsplit, nbh), dim3(256), 0, st, a);
     hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(nbh), dim3(128), 0, st, a.part_o, a.part_lse,
                        (float*)a.o, a.lse, a.D, a.nsplit);
   } else {
-    hipLaunchKernelGGL(decode_qprep_kernel<uint16_t>, dim3(nbh), dim3(64), 0, st,
-                       (const uint16_t*)a.q, (uint16_t*)a.qv, a.D, a.c, a.s, qpos, a.base);
+    hipLaunchKernelGGL(decode_qprep_kernel<uint16_t>, dim3(nbh), dim3(64), 0, st, a);
     const int G = a.Hq / a.Hkv;
     const int nqg = (G + 31) / 32;
     const dim3 grid((unsigned)((a.nsplit + 3) / 4), (unsigned)(a.B * a.Hkv * nqg));

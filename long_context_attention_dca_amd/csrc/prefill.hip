@@ -102,14 +102,22 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     hq = rem - b * a.Hq;
   }
   const int qt = nqt - 1 - qt_rank;
+  // This sequence's query rows sit at positions q0 .. q0 + nrows - 1 and see
+  // the keys [0, q0 + nrows).
+  int q0 = 0, nrows = a.L;
+  if (a.per_seq) {
+    q0 = a.seq_q0[b];
+    nrows = a.seq_len[b];
+  }
+  if (qt * BR >= nrows) return;   // whole workgroup, before any barrier
   const int g = hq / G;
   const int64_t bg = (int64_t)b * a.Hkv + g;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, ql = lane & 31;
-  const int L = a.L, s = a.s, c = a.c;
-  const int i0 = qt * BR;
+  const int L = q0 + nrows, s = a.s, c = a.c;
+  const int i0 = q0 + qt * BR;
   const int qrow = i0 + wave * 32 + ql;
   const int i_lo = i0 + wave * 32;
   const int i_hi = min(i_lo + 31, L - 1);
@@ -119,7 +127,8 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const int last_key = min(i0 + BR - 1, L - 1);
   const int nkt = last_key / BC + 1;
 
-  const uint16_t* qsrc = (const uint16_t*)a.q + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+  const int64_t qoff = (int64_t)b * a.q_rows + (qrow - q0);   // row in q / o
+  const uint16_t* qsrc = (const uint16_t*)a.q + (qoff * a.Hq + hq) * D;
   const uint16_t* kbase = (const uint16_t*)a.krot + bg * (int64_t)a.Lp * D;
   const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
 
@@ -321,7 +330,7 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qrow < L) {
     const float inv = 1.f / l_tot;
-    uint16_t* dst = (uint16_t*)a.o + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+    uint16_t* dst = (uint16_t*)a.o + (qoff * a.Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -331,7 +340,8 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         wv.y = pack_bf16x2(oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv);
         *(uint2*)(dst + db * 32 + grp * 8 + hh * 4) = wv;
       }
-    if (hh == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
+    if (hh == 0 && a.lse)
+      a.lse[((int64_t)b * a.Hq + hq) * a.q_rows + (qrow - q0)] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -406,14 +416,23 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     hq = rem - b * a.Hq;
   }
   const int qt = nqt - 1 - qt_rank;
+  // This sequence's query rows sit at positions q0 .. q0 + nrows - 1 and see
+  // the keys [0, q0 + nrows).  (DCA here needs q0 % 32 == 0: every wave
+  // block inside one chunk.)
+  int q0 = 0, nrows = a.L;
+  if (a.per_seq) {
+    q0 = a.seq_q0[b];
+    nrows = a.seq_len[b];
+  }
+  if (qt * PP_BR >= nrows) return;   // whole workgroup, before any barrier
   const int64_t bg = (int64_t)b * a.Hkv + hq / G;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2;
   const int hh = lane >> 5, ql = lane & 31;
-  const int L = a.L, s = a.s, c = a.c;
-  const int i0 = qt * PP_BR;
+  const int L = q0 + nrows, s = a.s, c = a.c;
+  const int i0 = q0 + qt * PP_BR;
   const int i_lo = i0 + wave * 32;
   const int qrow = i_lo + ql;
   const int nq = i_lo / s;                 // the wave's 32 rows share one chunk
@@ -444,7 +463,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     return min(nq - (t * BC) / s, 2);
   };
 
-  const uint16_t* qsrc = (const uint16_t*)a.q + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+  const int64_t qoff = (int64_t)b * a.q_rows + (qrow - q0);   // row in q / o
+  const uint16_t* qsrc = (const uint16_t*)a.q + (qoff * a.Hq + hq) * D;
   const uint16_t* kbase = (const uint16_t*)a.krot + bg * (int64_t)a.Lp * D;
   const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
 
@@ -737,7 +757,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const float l_tot = sum_halves(l_run);
   if (qrow < L) {
     const float inv = 1.f / l_tot;
-    uint16_t* dst = (uint16_t*)a.o + (((int64_t)b * L + qrow) * a.Hq + hq) * D;
+    uint16_t* dst = (uint16_t*)a.o + (qoff * a.Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -747,7 +767,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         wv.y = pack_bf16x2(oacc[db][grp4 * 4 + 2] * inv, oacc[db][grp4 * 4 + 3] * inv);
         *(uint2*)(dst + db * 32 + grp4 * 8 + hh * 4) = wv;
       }
-    if (hh == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
+    if (hh == 0 && a.lse)
+      a.lse[((int64_t)b * a.Hq + hq) * a.q_rows + (qrow - q0)] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -768,12 +789,18 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
   __shared__ float vs[FBC][D];
   __shared__ float ps[FBR][FBC + 1];
   const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int L = a.L, s = a.s, c = a.c;
+  int q0 = 0, nrows = a.L;   // this sequence's query rows: positions q0 .. q0 + nrows - 1
+  if (a.per_seq) {
+    q0 = a.seq_q0[b];
+    nrows = a.seq_len[b];
+  }
+  if (qt * FBR >= nrows) return;   // whole workgroup, before any barrier
+  const int L = q0 + nrows, s = a.s, c = a.c;
   const int G = a.Hq / a.Hkv, g = hq / G;
   const int64_t bg = (int64_t)b * a.Hkv + g;
   const int tid = threadIdx.x;
   const int r = tid >> 4, kq = tid & 15;
-  const int i0 = qt * FBR, i = i0 + r;
+  const int i0 = q0 + qt * FBR, i = i0 + r;
   const float* q = (const float*)a.q;
   const float* krot = (const float*)a.krot + bg * (int64_t)a.Lp * D;
   const float* krot2 = (const float*)a.krot2 + bg * (int64_t)a.Lp * D;   // SelfExtend only
@@ -788,7 +815,7 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
       for (int cls = 0; cls < NV; ++cls) qv[cls][k][rr] = qv[cls][k + HALF][rr] = 0.f;
       continue;
     }
-    const float* src = q + (((int64_t)b * L + ii) * a.Hq + hq) * D;
+    const float* src = q + (((int64_t)b * a.q_rows + (ii - q0)) * a.Hq + hq) * D;
     const float x1 = src[k], x2 = src[k + HALF];
     const int rqq = ii % s;
 #pragma unroll
@@ -817,7 +844,7 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
       const int j = j0 + row;
       ks[row][d] = krot[(int64_t)j * D + d];
       if constexpr (MAP == kMapSelfExtend) ks2[row][d] = krot2[(int64_t)j * D + d];
-      vs[row][d] = (j < L) ? vraw[(((int64_t)b * L + j) * a.Hkv + g) * D + d] : 0.f;
+      vs[row][d] = (j < L) ? vraw[(((int64_t)b * a.v_rows + j) * a.Hkv + g) * D + d] : 0.f;
     }
     __syncthreads();
     float sc[2];
@@ -867,11 +894,11 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
     }
   }
   if (i < L) {
-    float* dst = (float*)a.o + (((int64_t)b * L + i) * a.Hq + hq) * D;
+    float* dst = (float*)a.o + (((int64_t)b * a.q_rows + (i - q0)) * a.Hq + hq) * D;
     const float inv = 1.f / l;
 #pragma unroll
     for (int u = 0; u < NO; ++u) dst[kq + 16 * u] = o[u] * inv;
-    if (kq == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * L + i] = m + logf(l);
+    if (kq == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq) * a.q_rows + (i - q0)] = m + logf(l);
   }
 }
 
@@ -880,10 +907,14 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   const int xcd_map = ((int64_t)a.B * a.Hkv) % 8 == 0 ? 1 : 0;
   const float scale_log2 = a.sm_scale * kLog2e;
-  if (a.map == kMapSelfExtend || a.s % BC == 0) {
-    // SelfExtend, or DCA with every wave block and key tile inside one chunk:
-    // ping-pong kernel
-    const int nqt = (a.L + PP_BR - 1) / PP_BR;
+  // DCA takes the ping-pong kernel when every 32-row wave block and 64-key
+  // tile lies inside one chunk: s a multiple of 64 and query offsets
+  // multiples of 32.  SelfExtend always does.
+  bool pp = a.s % BC == 0;
+  if (a.per_seq)
+    for (int i = 0; i < a.B; ++i) pp = pp && a.seq_q0[i] % 32 == 0;
+  if (a.map == kMapSelfExtend || pp) {
+    const int nqt = (a.q_rows + PP_BR - 1) / PP_BR;
     const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
     if (a.map == kMapSelfExtend) {
       if (a.D == 64)
@@ -898,7 +929,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  const int nqt = (a.L + BR - 1) / BR;
+  const int nqt = (a.q_rows + BR - 1) / BR;
   const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
   if (a.D == 64)
     hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(256), 0, st, a, nqt, xcd_map, scale_log2);
@@ -908,7 +939,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.L + FBR - 1) / FBR), (unsigned)a.Hq, (unsigned)a.B);
+  const dim3 grid((unsigned)((a.q_rows + FBR - 1) / FBR), (unsigned)a.Hq, (unsigned)a.B);
   if (a.map == kMapSelfExtend) {
     if (a.D == 64)
       hipLaunchKernelGGL((prefill_f32_kernel<64, kMapSelfExtend>), grid, dim3(256), 0, st, a);

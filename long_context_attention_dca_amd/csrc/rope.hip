@@ -109,32 +109,37 @@ hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int
 __device__ inline int vt_perm(int p) { return (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
 template <typename T, int D, bool TRANSPOSE_V>
-__global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                      const double2* __restrict__ table,
-                                                      T* __restrict__ krot, uint16_t* __restrict__ vt,
-                                                      T* __restrict__ k_rot_out, int L, int Lp, int Hkv,
-                                                      int kdiv, int kmod) {
+__global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
   constexpr int half = D / 2;
   constexpr int TK = kPrefillTileKeys;
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int j0 = tile * TK;
-  const int64_t bg = (int64_t)b * Hkv + g;
+  const int Lb = a.per_seq ? a.seq_len[b] : a.L;   // valid rows of this sequence
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const T* k = (const T*)a.k;
+  T* krot = (T*)a.krot;
+  T* k_rot_out = (T*)a.k_rot_out;
   for (int idx = threadIdx.x; idx < TK * half; idx += 256) {
     const int row = idx / half, kk = idx - row * half;
     const int j = j0 + row;
-    T* dst = krot + (bg * Lp + j) * D;
-    if (j < L) {
-      const int64_t in = (((int64_t)b * L + j) * Hkv + g) * D;
+    T* dst = krot + (bg * a.Lp + j) * D;
+    if (j < Lb) {
+      const int64_t in = (((int64_t)b * a.in_rows + j) * a.Hkv + g) * D;
       const double x1 = Elem<T>::load(k + in + kk);
       const double x2 = Elem<T>::load(k + in + kk + half);
-      const double2 a = table[((j / kdiv) % kmod) * half + kk];
-      const float y1 = (float)(x1 * a.x - x2 * a.y);
-      const float y2 = (float)(x2 * a.x + x1 * a.y);
-      Elem<T>::store(dst + kk, y1);
-      Elem<T>::store(dst + kk + half, y2);
-      if (k_rot_out) {
-        Elem<T>::store(k_rot_out + in + kk, y1);
-        Elem<T>::store(k_rot_out + in + kk + half, y2);
+      if (a.table) {
+        const double2 c = a.table[((j / a.kdiv) % a.kmod) * half + kk];
+        const float y1 = (float)(x1 * c.x - x2 * c.y);
+        const float y2 = (float)(x2 * c.x + x1 * c.y);
+        Elem<T>::store(dst + kk, y1);
+        Elem<T>::store(dst + kk + half, y2);
+        if (k_rot_out) {
+          Elem<T>::store(k_rot_out + in + kk, y1);
+          Elem<T>::store(k_rot_out + in + kk + half, y2);
+        }
+      } else {   // already rotated: exact copy
+        Elem<T>::store(dst + kk, (float)x1);
+        Elem<T>::store(dst + kk + half, (float)x2);
       }
     } else {
       Elem<T>::store(dst + kk, 0.f);
@@ -142,17 +147,17 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, c
     }
   }
   if constexpr (TRANSPOSE_V) {
-    if (vt == nullptr) return;   // uniform: a second key rotation without V
+    if (a.vt == nullptr) return;   // uniform: a second key rotation without V
     __shared__ uint16_t vs[TK][D + 2];
-    const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
+    const uint16_t* vv = reinterpret_cast<const uint16_t*>(a.v);
     for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
       const int row = idx / D, d = idx - row * D;
       const int j = j0 + row;
-      vs[row][d] = (j < L) ? vv[(((int64_t)b * L + j) * Hkv + g) * D + d] : (uint16_t)0;
+      vs[row][d] = (j < Lb) ? vv[(((int64_t)b * a.in_rows + j) * a.Hkv + g) * D + d] : (uint16_t)0;
     }
     __syncthreads();
-    const int ntiles = Lp / TK;
-    uint16_t* dst = vt + ((bg * ntiles + tile) * D) * TK;
+    const int ntiles = a.Lp / TK;
+    uint16_t* dst = (uint16_t*)a.vt + ((bg * ntiles + tile) * D) * TK;
     for (int idx = threadIdx.x; idx < D * TK; idx += 256) {
       const int d = idx / TK, p = idx - d * TK;
       dst[idx] = vs[vt_perm(p)][d];
@@ -160,29 +165,19 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(const T* __restrict__ k, c
   }
 }
 
-template <typename T, bool TV>
-static void launch_prep_t(int D, dim3 grid, hipStream_t st, const void* k, const void* v,
-                          const double2* table, void* krot, void* vt, void* k_rot_out, int L, int Lp,
-                          int Hkv, int kdiv, int kmod) {
-  if (D == 64)
-    hipLaunchKernelGGL((kv_prep_kernel<T, 64, TV>), grid, dim3(256), 0, st, (const T*)k, (const T*)v,
-                       table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, kdiv, kmod);
-  else
-    hipLaunchKernelGGL((kv_prep_kernel<T, 128, TV>), grid, dim3(256), 0, st, (const T*)k,
-                       (const T*)v, table, (T*)krot, (uint16_t*)vt, (T*)k_rot_out, L, Lp, Hkv, kdiv,
-                       kmod);
-}
-
-hipError_t launch_kv_prep(const void* k, const void* v, const double2* table, void* krot, void* vt,
-                          void* k_rot_out, int64_t B, int64_t L, int64_t Lp, int64_t Hkv, int64_t D,
-                          int kdiv, int kmod, int dtype, hipStream_t st) {
-  const dim3 grid((unsigned)(Lp / kPrefillTileKeys), (unsigned)Hkv, (unsigned)B);
-  if (dtype == 0)
-    launch_prep_t<float, false>((int)D, grid, st, k, v, table, krot, vt, k_rot_out, (int)L, (int)Lp,
-                                (int)Hkv, kdiv, kmod);
-  else
-    launch_prep_t<uint16_t, true>((int)D, grid, st, k, v, table, krot, vt, k_rot_out, (int)L,
-                                  (int)Lp, (int)Hkv, kdiv, kmod);
+hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st) {
+  const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)a.Hkv, (unsigned)a.B);
+  if (dtype == 0) {
+    if (a.D == 64)
+      hipLaunchKernelGGL((kv_prep_kernel<float, 64, false>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((kv_prep_kernel<float, 128, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.D == 64)
+      hipLaunchKernelGGL((kv_prep_kernel<uint16_t, 64, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((kv_prep_kernel<uint16_t, 128, true>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -213,3 +213,49 @@ def test_selfextend_rejects_before_touching_device(lib, over, status):
 def test_remap_selfextend_map_validation(lib, map_, c, w, status):
     # B = 0: a valid call is an empty no-op, so nothing reaches the device
     assert lib.dca_rope_remap(FAKE, FAKE, 0, 8, 2, 64, 0, map_, c, w, 1e4, 1, None) == status
+
+
+def _i64s(*vals):
+    import ctypes
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+CHUNK_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos0=(0, 64), q_len=None, B=2, Lq=64,
+                cache_len=256, Hq=4, Hkv=2, D=128, c=128, w=32, base=1e4, sm_scale=0.0, dtype=1,
+                ws=FAKE_WS, ws_bytes=1 << 30, stream=None)
+
+
+def call_chunk(lib, **over):
+    a = dict(CHUNK_OK, **over)
+    p0 = None if a["pos0"] is None else _i64s(*a["pos0"])
+    ql = None if a["q_len"] is None else _i64s(*a["q_len"])
+    return lib.dca_prefill_chunk(a["q"], a["k"], a["v"], a["o"], a["lse"], p0, ql, a["B"], a["Lq"],
+                                 a["cache_len"], a["Hq"], a["Hkv"], a["D"], a["c"], a["w"], a["base"],
+                                 a["sm_scale"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(pos0=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(pos0=(0, -1)), _lib.DCA_ERR_INVALID_ARG),
+    (dict(pos0=(0, 200)), _lib.DCA_ERR_INVALID_ARG),        # 200 + 64 > cache_len
+    (dict(q_len=(65, 1)), _lib.DCA_ERR_INVALID_ARG),        # more rows than Lq
+    (dict(q_len=(-1, 1)), _lib.DCA_ERR_INVALID_ARG),
+    (dict(Lq=300), _lib.DCA_ERR_INVALID_ARG),               # Lq > cache_len
+    (dict(k=None), _lib.DCA_ERR_INVALID_ARG),
+    (dict(w=128), _lib.DCA_ERR_INVALID_ARG),
+    (dict(D=96), _lib.DCA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=100), _lib.DCA_ERR_WORKSPACE),
+    (dict(q_len=(0, 0)), _lib.DCA_OK),                      # no rows: nothing enqueued
+])
+def test_prefill_chunk_validation(lib, over, status):
+    assert call_chunk(lib, **over) == status
+
+
+@pytest.mark.parametrize("kv,status", [((0, 5), _lib.DCA_ERR_INVALID_ARG), ((5, 1001), _lib.DCA_ERR_INVALID_ARG),
+                                       (None, _lib.DCA_ERR_INVALID_ARG)])
+def test_decode_varlen_validation(lib, kv, status):
+    arr = None if kv is None else _i64s(*kv)
+    assert lib.dca_decode_varlen(FAKE, FAKE, FAKE, FAKE, None, arr, 2, 1000, 8, 2, 64, 128, 32, 1e4, 0.0, 1,
+                                 FAKE_WS, 1 << 30, None) == status
+    assert lib.dca_decode_varlen(FAKE, FAKE, FAKE, FAKE, None, _i64s(5, 9), 2, 1000, 8, 2, 64, 128, 32, 1e4,
+                                 0.0, 1, FAKE_WS, 64, None) == _lib.DCA_ERR_WORKSPACE
