@@ -279,13 +279,15 @@ def main():
         del kcache, qchunk, cws, ochunk
     if run_decode and not args.no_chunked:
         kvr = [int(x) for x in np.linspace(DC["kv_len"] // 2, DC["kv_len"], DC["B"])]
-        dca.decode_varlen(dq, kc, vc, kvr, DC["c"], DC["w"], DC["base"], workspace=dws)
+        dvws = torch.empty(dca.decode_varlen_workspace_bytes(kvr, DC["Hq"], DC["Hkv"], DC["D"], torch.bfloat16),
+                           dtype=torch.uint8, device=dev)
+        dca.decode_varlen(dq, kc, vc, kvr, DC["c"], DC["w"], DC["base"], workspace=dvws)
         torch.cuda.synchronize()
         nd = max(1, min(args.steps, 10))
         dv = [events(2) for _ in range(nd)]
         for i in range(nd):
             dv[i][0].record()
-            dca.decode_varlen(dq, kc, vc, kvr, DC["c"], DC["w"], DC["base"], workspace=dws)
+            dca.decode_varlen(dq, kc, vc, kvr, DC["c"], DC["w"], DC["base"], workspace=dvws)
             dv[i][1].record()
         torch.cuda.synchronize()
         dv_ms = sum(e[0].elapsed_time(e[1]) for e in dv) / nd

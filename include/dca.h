@@ -268,12 +268,15 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
  *   kv_len   : HOST array of B lengths, 1 <= kv_len[b] <= cache_len (read
  *              during the call only).
  *   k_cache, v_cache : [B, cache_len, Hkv, D]; rows >= kv_len[b] are not read.
- *   ws       : at least dca_decode_workspace_bytes(B, max_b kv_len[b], Hq, Hkv,
- *              D, dtype) bytes.
- * Everything else as in dca_decode.  Key ranges past a sequence's end
+ *   ws       : at least dca_decode_varlen_workspace_bytes(kv_len, B, Hq, Hkv, D,
+ *              dtype) bytes (0 there on invalid sizes).
+ * Everything else as in dca_decode.  The key-range length spreads the whole
+ * batch's keys over one round of waves; ranges past a sequence's end
  * contribute nothing to the merge.  Larger batches are processed in groups
  * of 64 sequences.
  */
+size_t dca_decode_varlen_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
+                                         int64_t D, int dtype);
 int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                       const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
                       int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,

@@ -35,7 +35,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
            "selfextend_prefill", "prefill_chunk", "decode_varlen", "prefill_workspace_bytes", "decode_workspace_bytes",
-           "selfextend_workspace_bytes", "DCAError", "library_path"]
+           "selfextend_workspace_bytes", "decode_varlen_workspace_bytes", "DCAError", "library_path"]
 
 _DT = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}
 
@@ -277,6 +277,13 @@ def prefill_chunk(q, k_cache, v_cache, pos0, c: int, w: int, base: float = 10000
     return (o, lse) if return_lse else o
 
 
+def decode_varlen_workspace_bytes(kv_len, Hq, Hkv, D, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    n = len(kv_len) if not isinstance(kv_len, int) else 1
+    kl, _ = _host_i64(kv_len, n, "kv_len")
+    return int(_lib.load().dca_decode_varlen_workspace_bytes(kl, n, Hq, Hkv, D, code))
+
+
 def decode_varlen(q, k_cache, v_cache, kv_len, c: int, w: int, base: float = 10000.0,
                   sm_scale: float | None = None, return_lse: bool = False, workspace=None):
     """DCA decode of a ragged batch: sequence b holds kv_len[b] cached tokens (its new
@@ -294,7 +301,7 @@ def decode_varlen(q, k_cache, v_cache, kv_len, c: int, w: int, base: float = 100
     kl, klv = _host_i64(kv_len, B, "kv_len")
     o = torch.empty_like(q)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
-    nbytes = int(lib.dca_decode_workspace_bytes(B, max(klv), Hq, Hkv, D, code))
+    nbytes = int(lib.dca_decode_varlen_workspace_bytes(kl, B, Hq, Hkv, D, code))
     if nbytes == 0:
         raise ValueError("invalid decode sizes")
     ws = _workspace(nbytes, q.device, workspace)

@@ -46,6 +46,7 @@ SIGNATURES = {
     "dca_prefill_chunk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64, _i64,
                                  _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "dca_decode_varlen_workspace_bytes": (_sz, [_i64p, _i64, _i64, _i64, _i64, _int]),
     "dca_decode_varlen": (_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _int, _int,
                                  _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _dbl,

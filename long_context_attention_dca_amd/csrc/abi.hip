@@ -79,13 +79,15 @@ struct DecodeLayout {
   size_t qv, part_o, part_lse, total;
 };
 
-bool decode_layout(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D, int dtype,
-                   DecodeLayout* out) {
+// kv: per-sequence cached key counts (host), or null for B sequences of
+// kv_len keys; kv_len is the longest sequence either way.
+bool decode_layout(int64_t B, const int64_t* kv, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
+                   int dtype, DecodeLayout* out) {
   if (B < 1 || kv_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D) || !dtype_ok(dtype))
     return false;
   if (B >= kMaxDim || kv_len >= kMaxDim / 2 || Hq >= 65536 || B * Hq >= kMaxDim) return false;
   DecodeLayout p;
-  decode_plan(B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
+  decode_plan(kv, B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
   p.qv = 0;
   p.part_o = (size_t)round_up(B * Hq * 3 * D * elem_size(dtype), 256);
   p.part_lse = p.part_o + (size_t)round_up(B * Hq * (int64_t)p.ns * D * 4, 256);
@@ -336,7 +338,7 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
 size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
                                   int dtype) {
   DecodeLayout p;
-  return decode_layout(B, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+  return decode_layout(B, nullptr, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
 }
 
 int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -351,7 +353,7 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
       (lse && !aligned(lse, 4)))
     return DCA_ERR_INVALID_ARG;
   DecodeLayout p;
-  if (!decode_layout(B, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!decode_layout(B, nullptr, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
@@ -464,6 +466,18 @@ int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
   return DCA_OK;
 }
 
+size_t dca_decode_varlen_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
+                                         int64_t D, int dtype) {
+  if (!kv_len || B < 1 || B >= kMaxDim) return 0;
+  int64_t max_kv = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    if (kv_len[b] < 1 || kv_len[b] >= kMaxDim / 2) return 0;
+    max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
+  }
+  DecodeLayout p;
+  return decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+}
+
 int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                       const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
                       int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
@@ -482,7 +496,7 @@ int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, v
     max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
   }
   DecodeLayout p;
-  if (!decode_layout(B, max_kv, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
   uint8_t* base = (uint8_t*)ws;
   const int64_t es = elem_size(dtype);

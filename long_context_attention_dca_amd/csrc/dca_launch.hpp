@@ -99,11 +99,17 @@ struct DecodeArgs {
   int cache_len;
   int per_seq;
   int seq_len[kMaxSeqGroup];
+  // bf16 split kernel: waves are numbered flat over the real (sequence, unit,
+  // key range) items; sequence b's waves start at wave_start[b] (set by the
+  // launcher).
+  int wave_start[kMaxSeqGroup + 1];
 };
 
-// Split plan shared by the workspace query and the launcher.
-void decode_plan(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int dtype, int* keys_per_split,
-                 int* nsplit);
+// Split plan shared by the workspace queries and the launchers: kv holds the
+// B sequences' cached key counts (host memory), or is null for B sequences
+// of uniform_kv keys.
+void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv, int dtype,
+                 int* keys_per_split, int* nsplit);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
 
 }  // namespace dca

@@ -88,12 +88,26 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, ql = lane & 31;
-  const int split = blockIdx.x * 4 + wave;
-  if (split >= a.nsplit) return;
-  const int unit = blockIdx.y;  // (b, g, query group)
+  // Flat wave index -> (sequence b, unit (KV head g, query group qg), key
+  // range).  Only real ranges get a wave: sequence b has ceil(keys / kps)
+  // ranges for each of its Hkv * nqg units.
+  const int f = blockIdx.x * 4 + wave;
+  const int upq = a.Hkv * nqg;
+  int b = 0, rem;
+  if (a.per_seq) {
+    if (f >= a.wave_start[a.B]) return;
+    while (b + 1 < a.B && a.wave_start[b + 1] <= f) ++b;   // wave-uniform scalar loop
+    rem = f - a.wave_start[b];
+  } else {
+    if (f >= a.B * upq * a.nsplit) return;
+    b = f / (upq * a.nsplit);
+    rem = f - b * upq * a.nsplit;
+  }
+  const int nspl = (seq_keys(a, b) + a.keys_per_split - 1) / a.keys_per_split;
+  const int unit = rem / nspl;
+  const int split = rem - unit * nspl;
   const int qg = unit % nqg;
-  const int bg = unit / nqg;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int g = unit / nqg;
   const int G = a.Hq / a.Hkv;
   const int qi = qg * 32 + ql;   // index inside the GQA group
   const bool qvalid = qi < G;
@@ -351,16 +365,20 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
 
 // ---- 3. combine ----------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(128) decode_combine_kernel(const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_lse,
-                                                             T* __restrict__ o, float* __restrict__ lse, int D,
-                                                             int ns) {
+__global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
   // One workgroup per (batch, query head): the split weights 2^(lse_i - M)
-  // are computed once into LDS, then every thread sums one output dim.
+  // are computed once into LDS, then every thread sums one output dim.  Only
+  // the sequence's own key ranges are merged (ceil(keys / kps) of the nsplit
+  // slots).
   __shared__ float wts[kMaxSplits];
   __shared__ float red[2];
+  const float* __restrict__ part_o = a.part_o;
+  T* __restrict__ o = (T*)a.o;
+  float* __restrict__ lse = a.lse;
+  const int D = a.D;
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const float* pl = part_lse + (int64_t)bh * ns;
+  const int ns = (seq_keys(a, bh / a.Hq) + a.keys_per_split - 1) / a.keys_per_split;
+  const float* pl = a.part_lse + (int64_t)bh * a.nsplit;
   float M = -INFINITY;
   for (int i = tid; i < ns; i += 128) M = fmaxf(M, pl[i]);
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -379,7 +397,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const float* __rest
   __syncthreads();
   const float wsum = red[0] + red[1];
   if (tid < D) {
-    const float* po = part_o + (int64_t)bh * ns * D + tid;
+    const float* po = part_o + (int64_t)bh * a.nsplit * D + tid;
     float acc = 0.f;
     for (int i = 0; i < ns; ++i) acc = fmaf(wts[i], po[(int64_t)i * D], acc);
     Elem<T>::store(o + (int64_t)bh * D + tid, acc / wsum);
@@ -389,24 +407,44 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const float* __rest
 
 }  // namespace
 
-void decode_plan(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int dtype, int* keys_per_split,
-                 int* nsplit) {
+void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv, int dtype,
+                 int* keys_per_split, int* nsplit) {
+  // One wave per key range, as many ranges as the chip holds at once: MI355X
+  // runs 8 of these waves per CU (2 per SIMD) on 256 CUs.  The range length is
+  // the shortest multiple of 32 keys whose ranges, over the whole batch (a
+  // ragged one too), fit in one such round: one round of long ranges measured
+  // faster than several rounds of short ones (fewer prologues, partials and
+  // round boundaries), and a second, mostly idle round costs a whole range.
   const int64_t G = Hq / Hkv;
-  const int64_t units = dtype == 0 ? B * Hq : B * Hkv * ((G + 31) / 32);
-  // One wave per split, as many splits as the chip holds at once: MI355X runs
-  // 8 of these waves per CU (2 per SIMD) on 256 CUs.  One round of long splits
-  // measured faster than several rounds of short ones (fewer prologues,
-  // partials and round boundaries).
+  const int64_t waves_per_key = dtype == 0 ? Hq : Hkv * ((G + 31) / 32);  // waves reading one cached key
   const int64_t target = 2048;
-  int64_t per = (target + units - 1) / units;
-  if (per < 1) per = 1;
-  int64_t kps = (kv_len + per - 1) / per;
-  kps = kps < 256 ? 256 : kps;
-  // the combine kernel keeps one weight per split in LDS: at most kMaxSplits
-  const int64_t min_kps = (kv_len + kMaxSplits - 1) / kMaxSplits;
-  kps = round_up(kps < min_kps ? min_kps : kps, SUB);
+  auto len = [&](int64_t b) { return kv ? kv[b] : uniform_kv; };
+  int64_t max_kv = 0;
+  for (int64_t b = 0; b < B; ++b) max_kv = len(b) > max_kv ? len(b) : max_kv;
+  auto waves = [&](int64_t kps) {
+    if (!kv) return B * ((uniform_kv + kps - 1) / kps) * waves_per_key;
+    int64_t n = 0;
+    for (int64_t b = 0; b < B; ++b) n += (kv[b] + kps - 1) / kps;
+    return n * waves_per_key;
+  };
+  // Search in units of SUB keys.  At least 256 keys per range, and at most
+  // kMaxSplits ranges per sequence (the combine kernel keeps one weight per
+  // range in LDS).  waves() never grows with the range length; if even one
+  // range per sequence overflows the round, the whole length is taken.
+  int64_t lo = (max_kv + kMaxSplits - 1) / kMaxSplits;
+  lo = (round_up(lo < 256 ? 256 : lo, SUB)) / SUB;
+  int64_t hi = round_up(max_kv, SUB) / SUB;
+  if (hi < lo) hi = lo;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (waves(mid * SUB) <= target)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int64_t kps = lo * SUB;
   *keys_per_split = (int)kps;
-  *nsplit = (int)((kv_len + kps - 1) / kps);
+  *nsplit = (int)((max_kv + kps - 1) / kps);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
@@ -414,20 +452,27 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
   if (dtype == 0) {
     hipLaunchKernelGGL(decode_qprep_kernel<float>, dim3(nbh), dim3(64), 0, st, a);
     hipLaunchKernelGGL(decode_split_f32_kernel, dim3(a.nsplit, nbh), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(nbh), dim3(128), 0, st, a.part_o, a.part_lse,
-                       (float*)a.o, a.lse, a.D, a.nsplit);
+    hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(nbh), dim3(128), 0, st, a);
   } else {
     hipLaunchKernelGGL(decode_qprep_kernel<uint16_t>, dim3(nbh), dim3(64), 0, st, a);
     const int G = a.Hq / a.Hkv;
     const int nqg = (G + 31) / 32;
-    const dim3 grid((unsigned)((a.nsplit + 3) / 4), (unsigned)(a.B * a.Hkv * nqg));
+    DecodeArgs b = a;
+    int64_t waves = (int64_t)a.B * a.Hkv * nqg * a.nsplit;
+    if (a.per_seq) {   // flat numbering of the real ranges, sequence by sequence
+      b.wave_start[0] = 0;
+      for (int i = 0; i < a.B; ++i)
+        b.wave_start[i + 1] = b.wave_start[i] +
+                              (a.seq_len[i] + a.keys_per_split - 1) / a.keys_per_split * a.Hkv * nqg;
+      waves = b.wave_start[a.B];
+    }
+    const dim3 grid((unsigned)((waves + 3) / 4));
     const float scale_log2 = a.sm_scale * kLog2e;
     if (a.D == 64)
-      hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, dim3(256), 0, st, a, nqg, scale_log2);
+      hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, dim3(256), 0, st, b, nqg, scale_log2);
     else
-      hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, dim3(256), 0, st, a, nqg, scale_log2);
-    hipLaunchKernelGGL(decode_combine_kernel<uint16_t>, dim3(nbh), dim3(128), 0, st, a.part_o,
-                       a.part_lse, (uint16_t*)a.o, a.lse, a.D, a.nsplit);
+      hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, dim3(256), 0, st, b, nqg, scale_log2);
+    hipLaunchKernelGGL(decode_combine_kernel<uint16_t>, dim3(nbh), dim3(128), 0, st, a);
   }
   return hipGetLastError();
 }

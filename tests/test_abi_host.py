@@ -259,3 +259,14 @@ def test_decode_varlen_validation(lib, kv, status):
                                  FAKE_WS, 1 << 30, None) == status
     assert lib.dca_decode_varlen(FAKE, FAKE, FAKE, FAKE, None, _i64s(5, 9), 2, 1000, 8, 2, 64, 128, 32, 1e4,
                                  0.0, 1, FAKE_WS, 64, None) == _lib.DCA_ERR_WORKSPACE
+
+
+def test_decode_varlen_workspace_sizes(lib):
+    # uniform lengths give the uniform layout
+    assert lib.dca_decode_varlen_workspace_bytes(_i64s(*([100001] * 16)), 16, 64, 8, 128, 1) == \
+        lib.dca_decode_workspace_bytes(16, 100001, 64, 8, 128, 1)
+    # a ragged batch spreads its keys: at least as many ranges for the longest sequence
+    ragged = lib.dca_decode_varlen_workspace_bytes(_i64s(*([1000] * 15 + [100001])), 16, 64, 8, 128, 1)
+    assert ragged >= lib.dca_decode_workspace_bytes(16, 100001, 64, 8, 128, 1)
+    assert lib.dca_decode_varlen_workspace_bytes(_i64s(5, 0), 2, 8, 2, 64, 1) == 0
+    assert lib.dca_decode_varlen_workspace_bytes(None, 2, 8, 2, 64, 1) == 0
