@@ -38,3 +38,10 @@ from .selfextend_ref import (  # noqa: F401
     selfextend_prefill_ref,
     selfextend_prefill_formB,
 )
+from .coarse_fine_ref import (  # noqa: F401
+    coarse_fine_distance_table,
+    coarse_fine_positions,
+    coarse_fine_key_positions,
+    coarse_fine_prefill_ref,
+    coarse_fine_prefill_formB,
+)
