@@ -118,7 +118,8 @@ def main():
     ap.add_argument("--no-selfextend", action="store_true", help="skip the SelfExtend 32k prefill")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked 32k prefill and the ragged 100k decode")
-    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k", "selfextend"], default=None,
+    ap.add_argument("--no-coarse-fine", action="store_true", help="skip the coarse / fine map 32k prefill")
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k", "selfextend", "coarsefine"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
@@ -156,6 +157,8 @@ def main():
     run_128k = (args.only == "prefill128k") or (args.only is None and not args.no_128k)
     SE = inputs.WORKLOADS["selfextend_70b_32k"]
     run_se = (args.only == "selfextend") or (args.only is None and not args.no_selfextend)
+    CF = inputs.WORKLOADS["coarse_fine_70b_32k"]
+    run_cf = (args.only == "coarsefine") or (args.only is None and not args.no_coarse_fine)
 
     # ---------------- inputs, resident in HBM before timing ----------------
     if run_prefill:
@@ -330,6 +333,42 @@ def main():
                                 "prefill": {k_: SE[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "group",
                                                                   "window")}}
         del sq, sk, sv, sws
+        torch.cuda.empty_cache()
+
+    # ---------------- coarse / fine map 32k prefill (reported beside the step) --
+    if run_cf:
+        log("generating coarse_fine_70b_32k inputs")
+        cq_h, ck_h, cv_h = inputs.prefill_inputs(CF["B"], CF["L"], CF["Hq"], CF["Hkv"], CF["D"], "bf16",
+                                                 CF["seed"])
+        cq, ck, cv = cq_h.to(dev), ck_h.to(dev), cv_h.to(dev)
+        del cq_h, ck_h, cv_h
+        cws = torch.empty(dca.coarse_fine_workspace_bytes(CF["B"], CF["L"], CF["Hkv"], CF["D"], torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        cf_call = lambda: dca.coarse_fine_prefill(cq, ck, cv, CF["chunk"], CF["train_len"], CF["target_len"],
+                                                  CF["base"], workspace=cws)
+        for _ in range(max(1, args.warmup)):
+            cf_call()
+        torch.cuda.synchronize()
+        ncf = max(1, min(args.steps, 5))
+        cfev = [events(2) for _ in range(ncf)]
+        for i in range(ncf):
+            cfev[i][0].record()
+            cf_call()
+            cfev[i][1].record()
+        torch.cuda.synchronize()
+        cf_ms = sum(e[0].elapsed_time(e[1]) for e in cfev) / ncf
+        fl = prefill_flops(CF["B"], CF["L"], CF["Hq"], CF["D"])
+        result["coarse_fine_32k"] = {"ms": cf_ms, "tflops": fl / (cf_ms * 1e-3) / 1e12,
+                                     "frac": fl / (cf_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                     "chunk": CF["chunk"], "train_len": CF["train_len"],
+                                     "target_len": CF["target_len"], "steps": ncf,
+                                     "includes": "theta table, both key rotations, V layout, attention"}
+        if args.only == "coarsefine":
+            result["value"], result["unit"] = result["coarse_fine_32k"]["tflops"], "TFLOP/s"
+            result["config"] = {"workload": "coarse_fine_70b_32k",
+                                "prefill": {k_: CF[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "chunk",
+                                                                  "train_len", "target_len")}}
+        del cq, ck, cv, cws
         torch.cuda.empty_cache()
 
     # ---------------- 128k prefill (reported beside the step) ----------------

@@ -159,6 +159,40 @@ int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L,
                        const void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The DCA guide's own coarse / fine distances as an alternative position map.
+ *
+ * Definition: "Dual-Chunk Attention: Training-Free 100k+ Context Guide",
+ * sections "Inter-Chunk Attention" and "Successive Chunk Smoothing".  Chunk
+ * size C, chunk index c_x = floor(x / C), offset o_x = x mod C, and
+ * kappa = target_len / train_len.  For a causal pair (j <= i):
+ *   same chunk       : i - j
+ *   chunks >= 2 apart: (c_i - c_j) * C / kappa + (o_i - o_j)
+ *   adjacent chunks  : (1 - lambda)(i - j) + lambda * (the inter value),
+ *                      lambda = o_i / C
+ * The distances are real numbers, and the rotation angle of a pair is its
+ * distance times theta_k.  They are used as stated, not clamped: the map
+ * goes negative when o_j > o_i across several chunks, and can pass
+ * train_len past L = target_len.  The kernels factor each distance into a
+ * query position minus a key position:
+ *   keys at j (same or adjacent chunk) or at c_j C / kappa + o_j (older);
+ *   queries at i, i - o_i (1 - 1/kappa) or c_i C / kappa + o_i.
+ * These positions and their cos / sin are evaluated in fp64.
+ *
+ * dca_coarse_fine_workspace_bytes: scratch for the fp64 theta table, the two
+ * key rotations and the V layout (0 on invalid sizes).
+ * dca_coarse_fine_prefill: q [B, L, Hq, D], k / v [B, L, Hkv, D] raw; o, lse,
+ *   sm_scale, GQA, dtypes as in dca_prefill.  chunk >= 1, train_len >= 1,
+ *   target_len >= 1.  bf16 needs chunk to be a multiple of 64, so that every
+ *   key tile has one relation; otherwise DCA_ERR_UNSUPPORTED.  fp32 takes
+ *   any chunk.
+ */
+size_t dca_coarse_fine_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype);
+int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                            int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int chunk, int train_len,
+                            int target_len, double rope_base, float sm_scale, int dtype, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * dca_prefill_chunk - DCA causal prefill of one chunk of new tokens per
  * sequence, over a KV cache that already holds the sequence's earlier tokens
  * (chunked prefill; ragged batches).

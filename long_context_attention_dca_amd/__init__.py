@@ -14,6 +14,8 @@ Entry points (same names as include/dca.h):
          return_lse=False, workspace=None)
   selfextend_prefill(q, k, v, group, window, base=1e4, sm_scale=None,
                      return_lse=False, workspace=None)
+  coarse_fine_prefill(q, k, v, chunk, train_len, target_len, base=1e4,
+                      sm_scale=None, return_lse=False, workspace=None)
   prefill_chunk(q, k_cache, v_cache, pos0, c, w, base=1e4, sm_scale=None,
                 q_len=None, return_lse=False, out=None, workspace=None)
   decode_varlen(q, k_cache, v_cache, kv_len, c, w, base=1e4, sm_scale=None,
@@ -34,7 +36,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
-           "selfextend_prefill", "prefill_chunk", "decode_varlen", "prefill_workspace_bytes", "decode_workspace_bytes",
+           "selfextend_prefill", "prefill_chunk", "decode_varlen", "coarse_fine_prefill", "prefill_workspace_bytes", "decode_workspace_bytes",
            "selfextend_workspace_bytes", "decode_varlen_workspace_bytes", "DCAError", "library_path"]
 
 _DT = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}
@@ -84,6 +86,11 @@ def decode_workspace_bytes(B, kv_len, Hq, Hkv, D, dtype) -> int:
 def selfextend_workspace_bytes(B, L, Hkv, D, group, window, dtype) -> int:
     code = dtype if isinstance(dtype, int) else _DT[dtype]
     return int(_lib.load().dca_selfextend_workspace_bytes(B, L, Hkv, D, group, window, code))
+
+
+def coarse_fine_workspace_bytes(B, L, Hkv, D, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(_lib.load().dca_coarse_fine_workspace_bytes(B, L, Hkv, D, code))
 
 
 def _workspace(nbytes: int, device, workspace):
@@ -308,5 +315,32 @@ def decode_varlen(q, k_cache, v_cache, kv_len, c: int, w: int, base: float = 100
     _lib.check("dca_decode_varlen", lib.dca_decode_varlen(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), _ptr(lse), kl,
         B, cache_len, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def coarse_fine_prefill(q, k, v, chunk: int, train_len: int, target_len: int, base: float = 10000.0,
+                        sm_scale: float | None = None, return_lse: bool = False, workspace=None):
+    """Causal prefill under the DCA guide's coarse / fine distance map (chunk size,
+    coarse distance scaled by train_len / target_len, lambda ramp for adjacent chunks).
+    q [B, L, Hq, D], k/v [B, L, Hkv, D] raw; returns o (and lse)."""
+    lib = _lib.load()
+    _check(q, "q", 4)
+    _check(k, "k", 4, q.dtype)
+    _check(v, "v", 4, q.dtype)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, L, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    code = _dtype_code(q)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, L, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(lib.dca_coarse_fine_workspace_bytes(B, L, Hkv, D, code))
+    if nbytes == 0:
+        raise ValueError("invalid coarse / fine prefill sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_coarse_fine_prefill", lib.dca_coarse_fine_prefill(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, L, Hq, Hkv, D,
+        chunk, train_len, target_len, float(base), float(sm_scale or 0.0), code,
         ws.data_ptr(), nbytes, _stream(q.device)))
     return (o, lse) if return_lse else o

@@ -43,6 +43,9 @@ SIGNATURES = {
     "dca_selfextend_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _int]),
     "dca_selfextend_prefill": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int,
                                       _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_coarse_fine_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int]),
+    "dca_coarse_fine_prefill": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int,
+                                       _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_prefill_chunk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64, _i64,
                                  _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),

@@ -335,6 +335,101 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }
 
+// Coarse / fine map workspace: theta_k table (512 B) | keys at their plain
+// positions | keys at the coarse-scaled positions | V (bf16: tiled transpose;
+// fp32: unused).
+constexpr size_t kThetaBytes = 512;   // D/2 <= 64 doubles
+
+static bool cf_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype, int64_t* Lp, size_t* krot2,
+                      size_t* vt, size_t* total) {
+  if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype)) return false;
+  if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
+  *Lp = round_up(L, kPrefillTileKeys);
+  const int64_t kbytes = round_up(B * Hkv * *Lp * D * elem_size(dtype), 256);
+  *krot2 = kThetaBytes + (size_t)kbytes;
+  *vt = kThetaBytes + (size_t)(2 * kbytes);
+  *total = kThetaBytes + (size_t)(3 * kbytes);
+  return true;
+}
+
+size_t dca_coarse_fine_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype) {
+  int64_t Lp;
+  size_t k2, vt, total;
+  return cf_layout(B, L, Hkv, D, dtype, &Lp, &k2, &vt, &total) ? total : 0;
+}
+
+int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                            int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int chunk, int train_len,
+                            int target_len, double rope_base, float sm_scale, int dtype, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16) || !base_ok(rope_base) ||
+      !attend_args_ok(q, o, lse, B, L, Hq, Hkv, sm_scale))
+    return DCA_ERR_INVALID_ARG;
+  if (chunk < 1 || chunk > (1 << 24) || train_len < 1 || target_len < 1) return DCA_ERR_INVALID_ARG;
+  // bf16 runs the two-group kernel: every 32-row block and 64-key tile inside one chunk
+  if (dtype == DCA_BF16 && chunk % kPrefillTileKeys != 0) return DCA_ERR_UNSUPPORTED;
+  int64_t Lp;
+  size_t off_k2, off_vt, total;
+  if (!cf_layout(B, L, Hkv, D, dtype, &Lp, &off_k2, &off_vt, &total)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  const double inv_kappa = (double)train_len / (double)target_len;
+  double* theta = (double*)base;
+  if (launch_rope_theta(theta, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  // keys at plain positions (with the V layout), then at coarse-scaled positions
+  KvPrepArgs kp = {};
+  kp.k = k;
+  kp.v = v;
+  kp.table = nullptr;
+  kp.krot = base + kThetaBytes;
+  kp.vt = dtype == DCA_BF16 ? base + off_vt : nullptr;
+  kp.B = (int)B;
+  kp.in_rows = (int)L;
+  kp.L = (int)L;
+  kp.Lp = (int)Lp;
+  kp.Hkv = (int)Hkv;
+  kp.D = (int)D;
+  kp.kdiv = 1;
+  kp.kmod = 1 << 30;
+  kp.pos_mode = 1;
+  kp.cf_chunk = chunk;
+  kp.cf_step = (double)chunk;
+  kp.theta = theta;
+  if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
+  kp.krot = base + off_k2;
+  kp.vt = nullptr;
+  kp.cf_step = (double)chunk * inv_kappa;
+  if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
+  PrefillArgs a = {};
+  a.q = q;
+  a.krot = base + kThetaBytes;
+  a.krot2 = base + off_k2;
+  a.vt = dtype == DCA_BF16 ? (const void*)(base + off_vt) : v;   // fp32 reads V as given
+  a.table = nullptr;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.L = (int)L;
+  a.Lp = (int)Lp;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.D = (int)D;
+  a.c = chunk;   // the chunk relation uses chunk size C (held in c and s)
+  a.w = 0;
+  a.s = chunk;
+  a.map = kMapCoarseFine;
+  a.se_group = 1;
+  a.q_rows = (int)L;
+  a.per_seq = 0;
+  a.v_rows = (int)L;
+  a.cf_inv_kappa = inv_kappa;
+  a.theta = theta;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+  return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
+}
+
 size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
                                   int dtype) {
   DecodeLayout p;

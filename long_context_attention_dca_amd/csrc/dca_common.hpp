@@ -28,6 +28,84 @@ __host__ __device__ inline int query_pos(int cls, int r, int s, int c) {
 // at floor(i / G) + W - floor(W / G), so their distance is at least W.
 __host__ __device__ inline int se_query_pos_grouped(int i, int G, int W) { return i / G + W - W / G; }
 
+// The DCA guide's coarse / fine distances ("Inter-Chunk Attention" and
+// "Successive Chunk Smoothing") factor into query minus key positions, with
+// chunk size C, offset o = x mod C and kappa = L_target / L_train:
+//   keys:    plain j (same or adjacent chunk), floor(j/C) C / kappa + o_j (older)
+//   queries: i (same chunk), i - o_i (1 - 1/kappa) (adjacent), floor(i/C) C / kappa + o_i.
+// Positions are real numbers (fp64).
+__host__ __device__ inline double cf_query_pos(int cls, int i, int C, double inv_kappa) {
+  const int o = i % C;
+  if (cls == 0) return (double)i;
+  if (cls == 1) return (double)i - (double)o * (1.0 - inv_kappa);
+  return (double)(i / C) * (double)C * inv_kappa + (double)o;
+}
+
+// sin and cos in fp64 without a library call (inlined, no stack): Cody-Waite
+// reduction x = n (pi/2) + r with pi/2 split into three parts (the first two
+// hold 33 significant bits each, so n * part is exact for n < 2^20; fma keeps
+// the reduction accurate beyond), then Taylor series on |r| <= pi/4 up to
+// r^17 / r^18 (truncation below 1e-19).  The split was computed from pi to
+// 130 digits (Machin's formula).  Used for RoPE angles of real-valued
+// positions.
+__host__ __device__ inline void dca_sincos(double x, double* s, double* c) {
+  constexpr double kTwoOverPi = 0.6366197723675814;
+  constexpr double kP1 = 1.5707963267341256;       // pi/2, first 33 bits
+  constexpr double kP2 = 6.077100506303966e-11;    // next 33 bits
+  constexpr double kP3 = 2.0222662487959506e-21;   // remainder
+  const double n = rint(x * kTwoOverPi);
+  double r = fma(-n, kP1, x);
+  r = fma(-n, kP2, r);
+  r = fma(-n, kP3, r);
+  const double r2 = r * r;
+  // 1/k! for the odd (sin) and even (cos) terms, Horner from the highest
+  constexpr double f3 = 1.0 / 6.0, f5 = f3 / 20.0, f7 = f5 / 42.0, f9 = f7 / 72.0, f11 = f9 / 110.0,
+                   f13 = f11 / 156.0, f15 = f13 / 210.0, f17 = f15 / 272.0;
+  constexpr double f2 = 0.5, f4 = f2 / 12.0, f6 = f4 / 30.0, f8 = f6 / 56.0, f10 = f8 / 90.0,
+                   f12 = f10 / 132.0, f14 = f12 / 182.0, f16 = f14 / 240.0, f18 = f16 / 306.0;
+  double ps = -f17;
+  ps = fma(ps, r2, f15);
+  ps = fma(ps, r2, -f13);
+  ps = fma(ps, r2, f11);
+  ps = fma(ps, r2, -f9);
+  ps = fma(ps, r2, f7);
+  ps = fma(ps, r2, -f5);
+  ps = fma(ps, r2, f3);
+  const double sr = fma(-ps * r2, r, r);          // r - r^3/3! + ...
+  double pc = f18;
+  pc = fma(pc, r2, -f16);
+  pc = fma(pc, r2, f14);
+  pc = fma(pc, r2, -f12);
+  pc = fma(pc, r2, f10);
+  pc = fma(pc, r2, -f8);
+  pc = fma(pc, r2, f6);
+  pc = fma(pc, r2, -f4);
+  pc = fma(pc, r2, f2);
+  const double cr = fma(-pc, r2, 1.0);            // 1 - r^2/2! + ...
+  const long long q = (long long)n & 3;
+  if (q == 0) {
+    *s = sr;
+    *c = cr;
+  } else if (q == 1) {
+    *s = cr;
+    *c = -sr;
+  } else if (q == 2) {
+    *s = -sr;
+    *c = -cr;
+  } else {
+    *s = -cr;
+    *c = sr;
+  }
+}
+
+// cos / sin of a real position p times theta_k (theta from a precomputed
+// table, so no library call is made), in fp64.
+__device__ inline double2 rope_cs(double p, double theta) {
+  double sn, cs;
+  dca_sincos(p * theta, &sn, &cs);
+  return make_double2(cs, sn);
+}
+
 // ---- bf16 <-> fp32 -----------------------------------------------------------
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 

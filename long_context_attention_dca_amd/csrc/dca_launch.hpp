@@ -16,6 +16,8 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // RoPE cos/sin table [npos][D/2] of double2 (cos, sin), all in fp64.
 hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipStream_t st);
+// theta_k = base^(-2k/D) for k < D/2, fp64 (for real-valued positions).
+hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st);
 
 // dca_rope_remap kernel (dtype 0 = fp32, 1 = bf16).
 hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
@@ -39,6 +41,13 @@ struct KvPrepArgs {
   int B, in_rows, L, Lp, Hkv, D, kdiv, kmod;
   int per_seq;          // 1: seq_len[b] valid rows per sequence (else L)
   int seq_len[kMaxSeqGroup];
+  // pos_mode 1 (no cos/sin table): key j at floor(j / cf_chunk) * cf_step +
+  // j mod cf_chunk, a real number, with cos/sin made in fp64 from theta
+  // (cf_step = cf_chunk: plain positions; cf_chunk / kappa: coarse-scaled).
+  int pos_mode;
+  int cf_chunk;
+  double cf_step;
+  const double* theta;  // pos_mode 1: theta_k table [D/2]
 };
 hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st);
 
@@ -47,6 +56,9 @@ enum PosMap : int {
   kMapDCA = 0,         // chunk relation: intra / successive / inter queries, keys at j mod s
   kMapSelfExtend = 1,  // neighbor (i - j < W): plain positions; grouped: keys j/G,
                        // queries i/G + W - W/G
+  kMapCoarseFine = 2,  // the DCA guide's own distances: chunk C (held in c and s),
+                       // coarse chunk distance scaled by 1/kappa for pairs >= 2
+                       // chunks apart, lambda ramp for adjacent chunks
 };
 // SelfExtend pair classes (the order the kernels visit them in).
 constexpr int kSeGrouped = 0;
@@ -74,6 +86,9 @@ struct PrefillArgs {
   int seq_q0[kMaxSeqGroup];
   int seq_len[kMaxSeqGroup];
   int v_rows;          // fp32 kernels: rows per sequence of the raw V in vt
+  // kMapCoarseFine: 1 / kappa = L_train / L_target.
+  double cf_inv_kappa;
+  const double* theta;  // theta_k table [D/2] for the fp64 rotations of real positions
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);

@@ -136,7 +136,7 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // Lane (query ql, half hh) holds dims d = ds*16 + hh*8 + e; the rotate-half
   // partner d + D/2 is in step ds + NDS/2 of the same lane.
   bf16x8 qf[NDS];
-  auto load_q = [&](int cls) {
+  auto load_q = [&](int cls) __attribute__((always_inline)) {
     const int P = query_pos(cls, rq, s, c);
     const double2* tb = a.table + (int64_t)P * (D / 2);
     if (qrow < L) {
@@ -446,6 +446,13 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // the window edge are visited twice, each time with the other class masked;
   // the class is the same for the whole workgroup, and selects the key
   // rotation staged and the query variant used.
+  // Coarse / fine: the same two passes, split by key rotation.  First every
+  // tile of a chunk at least two before the workgroup's last chunk (scaled
+  // keys, inter query), then every tile from the chunk before its first chunk
+  // on (plain keys; intra or successive query, chosen per wave).  A wave
+  // whose relation to a tile belongs to the other pass sees it fully masked.
+  // (A workgroup's 256 rows can span several chunks, so the key rotation
+  // cannot follow one wave's relation: every wave stages part of each tile.)
   int n_gr = 0, nb_begin = 0, nvt = nkt;
   if constexpr (MAP == kMapSelfExtend) {
     const int W = a.se_window;
@@ -453,14 +460,28 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     n_gr = i_top >= W ? (i_top - W) / BC + 1 : 0;
     nb_begin = max(i0 - W + 1, 0) / BC;
     nvt = n_gr + (W > 0 ? nkt - nb_begin : 0);
+  } else if constexpr (MAP == kMapCoarseFine) {
+    const int c_first = i0 / s, c_last = min(i0 + PP_BR - 1, L - 1) / s;
+    n_gr = c_last >= 2 ? (c_last - 1) * (s / BC) : 0;
+    nb_begin = max(c_first - 1, 0) * (s / BC);
+    nvt = n_gr + nkt - nb_begin;
   }
   auto tile_of = [&](int t) __attribute__((always_inline)) {
-    if constexpr (MAP == kMapSelfExtend) return t < n_gr ? t : nb_begin + (t - n_gr);
+    if constexpr (MAP != kMapDCA) return t < n_gr ? t : nb_begin + (t - n_gr);
     return t;
   };
+  // The query variant of virtual tile t for this wave.  Coarse / fine plain
+  // pass: intra (0) or successive (1) by the wave's chunk distance, clamped
+  // for masked tiles so the variant only moves inter -> successive -> intra.
   auto class_of = [&](int t) __attribute__((always_inline)) {
     if constexpr (MAP == kMapSelfExtend) return t < n_gr ? kSeGrouped : kSeNeighbor;
+    if constexpr (MAP == kMapCoarseFine) return t < n_gr ? 2 : min(max(nq - (tile_of(t) * BC) / s, 0), 1);
     return min(nq - (t * BC) / s, 2);
+  };
+  // Coarse / fine: does this wave keep virtual tile t at all (else p = 0)?
+  auto cf_keep = [&](int t) __attribute__((always_inline)) {
+    const int rho = nq - (tile_of(t) * BC) / s;
+    return t < n_gr ? rho >= 2 : (rho == 0 || rho == 1);
   };
 
   const int64_t qoff = (int64_t)b * a.q_rows + (qrow - q0);   // row in q / o
@@ -469,10 +490,13 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
 
   bf16x8 qf[NDS];
-  auto load_q = [&](int cls) {
-    int P;
+  auto load_q = [&](int cls) __attribute__((always_inline)) {
+    int P = 0;
+    double Pf = 0.0;   // coarse / fine map: a real position, cos/sin made in fp64
     if constexpr (MAP == kMapSelfExtend)
       P = cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window);
+    else if constexpr (MAP == kMapCoarseFine)
+      Pf = cf_query_pos(cls, qrow, c, a.cf_inv_kappa);
     else
       P = query_pos(cls, rq, s, c);
     const double2* tb = a.table + (int64_t)P * (D / 2);   // read only for rows < L
@@ -486,7 +510,11 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         unpack_bf16x8(u2, x2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const double2 t = tb[ds * 16 + hh * 8 + e];
+          double2 t;
+          if constexpr (MAP == kMapCoarseFine)
+            t = rope_cs(Pf, a.theta[ds * 16 + hh * 8 + e]);
+          else
+            t = tb[ds * 16 + hh * 8 + e];
           y1[e] = (float)((double)x1[e] * t.x - (double)x2[e] * t.y);
           y2[e] = (float)((double)x2[e] * t.x + (double)x1[e] * t.y);
         }
@@ -522,8 +550,9 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const uint32_t head_bytes = (uint32_t)((int64_t)a.Lp * D * 2);
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, kBufferWord3);
-  __amdgpu_buffer_rsrc_t krsrc2 = krsrc;   // SelfExtend: grouped keys (at floor(j / G))
-  if constexpr (MAP == kMapSelfExtend)
+  // SelfExtend: grouped keys (at floor(j / G)); coarse / fine: scaled keys
+  __amdgpu_buffer_rsrc_t krsrc2 = krsrc;
+  if constexpr (MAP != kMapDCA)
     krsrc2 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint16_t*)a.krot2 + bg * (int64_t)a.Lp * D), (short)0, head_bytes, kBufferWord3);
   auto issue_k = [&](int t) {
@@ -532,6 +561,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     __amdgpu_buffer_rsrc_t rs = krsrc;
     if constexpr (MAP == kMapSelfExtend)
       if (class_of(t) == kSeGrouped) rs = krsrc2;
+    if constexpr (MAP == kMapCoarseFine)
+      if (t < n_gr) rs = krsrc2;   // the scaled-key pass (same for every wave)
 #pragma unroll
     for (int i = 0; i < KPW; ++i)
       if (wave + 8 * i < Smem<D>::KPIECES)
@@ -599,6 +630,13 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         need = need || j0 < i_lo + 32 - W;
       }
     }
+    if constexpr (MAP == kMapCoarseFine) {
+      if (!cf_keep(t)) {
+        lo = 1;
+        hi = 0;
+        need = true;
+      }
+    }
     if (need) {
       const int jb = j0 + hh * 4;
 #pragma unroll
@@ -657,7 +695,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // Both groups execute the same number of barriers; each runs its own loop
   // so every iteration is straight-line code.  Tiles past a wave's last row
   // are processed fully masked (p = 0) rather than skipped.
-  auto prep_q = [&](int t) {
+  auto prep_q = [&](int t) __attribute__((always_inline)) {
     const int cls = class_of(t);
     if (cls != cur_cls) {
       load_q(cls);
@@ -785,7 +823,8 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
   constexpr int NV = MAP == kMapSelfExtend ? 2 : 3;   // query variants
   __shared__ float qv[NV][D][FBR];
   __shared__ float ks[FBC][D + 1];
-  __shared__ float ks2[MAP == kMapSelfExtend ? FBC : 1][D + 1];   // SelfExtend grouped keys
+  // second key rotation: SelfExtend grouped keys / coarse-fine scaled keys
+  __shared__ float ks2[MAP != kMapDCA ? FBC : 1][D + 1];
   __shared__ float vs[FBC][D];
   __shared__ float ps[FBR][FBC + 1];
   const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -820,12 +859,17 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
     const int rqq = ii % s;
 #pragma unroll
     for (int cls = 0; cls < NV; ++cls) {
-      int P;
-      if constexpr (MAP == kMapSelfExtend)
-        P = cls == kSeNeighbor ? ii : se_query_pos_grouped(ii, a.se_group, W);
-      else
-        P = query_pos(cls, rqq, s, c);
-      const double2 t = a.table[(int64_t)P * HALF + k];
+      double2 t;
+      if constexpr (MAP == kMapCoarseFine) {
+        t = rope_cs(cf_query_pos(cls, ii, c, a.cf_inv_kappa), a.theta[k]);
+      } else {
+        int P;
+        if constexpr (MAP == kMapSelfExtend)
+          P = cls == kSeNeighbor ? ii : se_query_pos_grouped(ii, a.se_group, W);
+        else
+          P = query_pos(cls, rqq, s, c);
+        t = a.table[(int64_t)P * HALF + k];
+      }
       qv[cls][k][rr] = (float)((double)x1 * t.x - (double)x2 * t.y);
       qv[cls][k + HALF][rr] = (float)((double)x2 * t.x + (double)x1 * t.y);
     }
@@ -843,7 +887,7 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
       const int row = idx / D, d = idx - row * D;
       const int j = j0 + row;
       ks[row][d] = krot[(int64_t)j * D + d];
-      if constexpr (MAP == kMapSelfExtend) ks2[row][d] = krot2[(int64_t)j * D + d];
+      if constexpr (MAP != kMapDCA) ks2[row][d] = krot2[(int64_t)j * D + d];
       vs[row][d] = (j < L) ? vraw[(((int64_t)b * a.v_rows + j) * a.Hkv + g) * D + d] : 0.f;
     }
     __syncthreads();
@@ -863,8 +907,9 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
           for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], kr[d], acc);
         } else {
           const int cls = min(nq - j / s, 2);
+          const float* kr = (MAP == kMapCoarseFine && cls == 2) ? ks2[key] : ks[key];
 #pragma unroll 8
-          for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], ks[key][d], acc);
+          for (int d = 0; d < D; ++d) acc = fmaf(qv[cls][d][r], kr[d], acc);
         }
         sc[e] = acc * a.sm_scale;
       }
@@ -913,7 +958,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   bool pp = a.s % BC == 0;
   if (a.per_seq)
     for (int i = 0; i < a.B; ++i) pp = pp && a.seq_q0[i] % 32 == 0;
-  if (a.map == kMapSelfExtend || pp) {
+  if (a.map == kMapCoarseFine && !pp) return hipErrorInvalidValue;   // needs chunk % 64 == 0 (host-checked)
+  if (a.map != kMapDCA || pp) {
     const int nqt = (a.q_rows + PP_BR - 1) / PP_BR;
     const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
     if (a.map == kMapSelfExtend) {
@@ -921,6 +967,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapSelfExtend>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
       else
         hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapSelfExtend>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+    } else if (a.map == kMapCoarseFine) {
+      if (a.D == 64)
+        hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapCoarseFine>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+      else
+        hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapCoarseFine>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
     } else {
       if (a.D == 64)
         hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapDCA>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
@@ -945,6 +996,11 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((prefill_f32_kernel<64, kMapSelfExtend>), grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((prefill_f32_kernel<128, kMapSelfExtend>), grid, dim3(256), 0, st, a);
+  } else if (a.map == kMapCoarseFine) {
+    if (a.D == 64)
+      hipLaunchKernelGGL((prefill_f32_kernel<64, kMapCoarseFine>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_f32_kernel<128, kMapCoarseFine>), grid, dim3(256), 0, st, a);
   } else {
     if (a.D == 64)
       hipLaunchKernelGGL((prefill_f32_kernel<64, kMapDCA>), grid, dim3(256), 0, st, a);

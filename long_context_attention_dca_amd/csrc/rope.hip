@@ -31,6 +31,16 @@ hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipSt
   return hipGetLastError();
 }
 
+__global__ void rope_theta_kernel(double* __restrict__ theta, int half, int D, double base) {
+  const int k = threadIdx.x;
+  if (k < half) theta[k] = pow(base, -2.0 * (double)k / (double)D);
+}
+
+hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st) {
+  hipLaunchKernelGGL(rope_theta_kernel, dim3(1), dim3(64), 0, st, theta, D / 2, D, base);
+  return hipGetLastError();
+}
+
 // ---- dca_rope_remap -----------------------------------------------------------------
 // One workgroup per token t: the 64 (or 32) angles of its position are made
 // once in fp64 and applied to every (batch, head) row of that token.
@@ -127,8 +137,11 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
       const int64_t in = (((int64_t)b * a.in_rows + j) * a.Hkv + g) * D;
       const double x1 = Elem<T>::load(k + in + kk);
       const double x2 = Elem<T>::load(k + in + kk + half);
-      if (a.table) {
-        const double2 c = a.table[((j / a.kdiv) % a.kmod) * half + kk];
+      if (a.table || a.pos_mode == 1) {
+        const double2 c = a.pos_mode == 1
+                              ? rope_cs((double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk),
+                                        a.theta[kk])
+                              : a.table[((j / a.kdiv) % a.kmod) * half + kk];
         const float y1 = (float)(x1 * c.x - x2 * c.y);
         const float y2 = (float)(x2 * c.x + x1 * c.y);
         Elem<T>::store(dst + kk, y1);

@@ -74,4 +74,8 @@ WORKLOADS = {
     # (the same local window as the DCA workloads).
     "selfextend_70b_32k": dict(kind="selfextend", dtype="bf16", B=1, L=32768, Hq=64, Hkv=8, D=128,
                                group=8, window=1024, base=10000.0, seed=5),
+    # The DCA guide's coarse / fine map with its own parameters (chunk 512,
+    # trained length 4096, target 32768) on the 70B 32k shape.
+    "coarse_fine_70b_32k": dict(kind="coarse_fine", dtype="bf16", B=1, L=32768, Hq=64, Hkv=8, D=128,
+                                chunk=512, train_len=4096, target_len=32768, base=10000.0, seed=6),
 }

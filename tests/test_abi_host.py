@@ -270,3 +270,16 @@ def test_decode_varlen_workspace_sizes(lib):
     assert ragged >= lib.dca_decode_workspace_bytes(16, 100001, 64, 8, 128, 1)
     assert lib.dca_decode_varlen_workspace_bytes(_i64s(5, 0), 2, 8, 2, 64, 1) == 0
     assert lib.dca_decode_varlen_workspace_bytes(None, 2, 8, 2, 64, 1) == 0
+
+
+def test_coarse_fine_workspace_and_validation(lib):
+    Lp = 128
+    kbytes = 2 * 3 * Lp * 128 * 2
+    assert lib.dca_coarse_fine_workspace_bytes(2, 100, 3, 128, 1) == 512 + 3 * kbytes   # theta table first
+    assert lib.dca_coarse_fine_workspace_bytes(2, 100, 3, 96, 1) == 0
+    ok = [FAKE, FAKE, FAKE, FAKE, None, 1, 256, 4, 2, 128, 512, 4096, 32768, 1e4, 0.0, 1, FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(0, None, -1), (10, 0, -1), (11, 0, -1), (12, -5, -1), (10, 96, -2), (9, 80, -2),
+                       (17, 64, -3), (13, 0.0, -1)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_coarse_fine_prefill(*a) == st, (i, bad)
