@@ -18,6 +18,9 @@ from .dca_ref import (  # noqa: F401
     dca_prefill_formB,
     dca_decode_ref,
     dca_prefill_chunk_ref,
+    paged_rows,
+    dca_decode_paged_ref,
+    dca_prefill_chunk_paged_ref,
     MAP_KEY,
     MAP_Q_INTRA,
     MAP_Q_SUCC,

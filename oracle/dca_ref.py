@@ -386,3 +386,62 @@ def dca_prefill_chunk_ref(q, k_raw, v, pos0, c: int, w: int, base: float = 10000
                 O[b, ri, hi] = o[0]
                 LSE[b, hi, ri] = lse[0]
     return O, LSE
+
+
+# ---- paged KV caches ----------------------------------------------------------------
+# A serving KV cache ("Dual-Chunk Attention: Training-Free 100k+ Context Guide",
+# "Strategic Recommendations": DCA paired with split-KV decoding in serving) is
+# often held in fixed-size pages.  The pages describe no page layout; the one
+# used here is the common block table: row j of sequence b sits at row j mod P
+# of page block_table[b][j // P] of a pool [num_pages, P, H, D].  Paging moves
+# rows and changes no arithmetic, so the paged results are the dense ones of
+# the gathered sequence.
+
+def paged_rows(pool, block_table, b: int, n: int) -> np.ndarray:
+    """Rows 0 .. n-1 of sequence b from a paged pool [num_pages, P, H, D]."""
+    pool = np.asarray(pool)
+    P = pool.shape[1]
+    j = np.arange(n)
+    pages = np.asarray(block_table)[b, j // P]
+    if np.any(pages < 0) or np.any(pages >= pool.shape[0]):
+        raise ValueError("block table entry outside the page pool")
+    return pool[pages, j % P]
+
+
+def dca_decode_paged_ref(q, k_pool_raw, v_pool, block_table, kv_len, c: int, w: int,
+                         base: float = 10000.0, sm_scale: float | None = None):
+    """Decode against a paged cache of *unrotated* keys: sequence b's cache is
+    its first kv_len[b] rows gathered through the block table; its query sits
+    at kv_len[b] - 1.  Returns O [B, Hq, D] and LSE [B, Hq]."""
+    q = _f64(q)
+    B, Hq, D = q.shape
+    O = np.zeros((B, Hq, D))
+    LSE = np.zeros((B, Hq))
+    for b in range(B):
+        n = int(kv_len[b])
+        kb = _f64(paged_rows(_f64(k_pool_raw), block_table, b, n))[None]
+        vb = _f64(paged_rows(_f64(v_pool), block_table, b, n))[None]
+        o, lse = dca_decode_ref(q[b: b + 1], kb, vb, c, w, base, sm_scale)
+        O[b], LSE[b] = o[0], lse[0]
+    return O, LSE
+
+
+def dca_prefill_chunk_paged_ref(q, k_pool_raw, v_pool, block_table, pos0, c: int, w: int,
+                                base: float = 10000.0, sm_scale: float | None = None, q_len=None):
+    """Chunked prefill over a paged cache of *unrotated* keys: sequence b's
+    keys 0 .. pos0[b] + q_len[b] - 1 are gathered through the block table, then
+    the chunk is the dense chunked prefill of that sequence."""
+    q = _f64(q)
+    B, Lq, Hq, D = q.shape
+    p0 = np.broadcast_to(np.asarray(pos0, dtype=np.int64), (B,))
+    ql = np.full(B, Lq, dtype=np.int64) if q_len is None else np.asarray(q_len, dtype=np.int64)
+    O = np.zeros((B, Lq, Hq, D))
+    LSE = np.full((B, Hq, Lq), -np.inf)
+    for b in range(B):
+        n = int(p0[b] + ql[b])
+        kb = _f64(paged_rows(_f64(k_pool_raw), block_table, b, n))[None]
+        vb = _f64(paged_rows(_f64(v_pool), block_table, b, n))[None]
+        o, lse = dca_prefill_chunk_ref(q[b: b + 1], kb, vb, [int(p0[b])], c, w, base, sm_scale,
+                                       q_len=[int(ql[b])])
+        O[b], LSE[b] = o[0], lse[0]
+    return O, LSE
