@@ -316,6 +316,43 @@ int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, v
                       int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
                       size_t ws_bytes, void* stream);
 
+/*
+ * Paged KV caches: dca_decode_paged and dca_prefill_chunk_paged.
+ *
+ * Definition: the same results as dca_decode_varlen and dca_prefill_chunk
+ * for the sequence whose cached row j is row j mod page_size of page
+ * block_table[b][j / page_size].  Paging moves rows only.  The pages describe
+ * no page layout; this block table is the common one of serving KV caches
+ * (the DCA guide's "Strategic Recommendations" pair DCA with split-KV
+ * decoding for serving long contexts).
+ *
+ *   k_pages, v_pages : page pools [num_pages, page_size, Hkv, D] (keys rotated
+ *              at j mod s, as for the dense caches).
+ *   block_table : DEVICE array int32 [B, max_blocks]: the page of each block of
+ *              page_size rows of each sequence.  Entries past a sequence's last
+ *              used block are not read.  An entry outside [0, num_pages) is
+ *              never dereferenced; the results of that sequence that would
+ *              use it become NaN (others of the same sequence may too).
+ *   page_size : a multiple of 16 (so every 16-row half of the decode kernel's
+ *              32-key sub-tiles lies inside one page).
+ *   kv_len / pos0 + q_len : at most max_blocks * page_size.
+ *   ws       : decode: dca_decode_varlen_workspace_bytes(kv_len, ...); chunk:
+ *              dca_prefill_workspace_bytes(B, max_b(pos0[b] + q_len[b]), ...).
+ * Everything else as in dca_decode_varlen / dca_prefill_chunk.  Pool rows that
+ * no table entry names are never read.
+ */
+int dca_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                     void* o, float* lse, const int64_t* kv_len, int64_t B, int64_t num_pages,
+                     int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv, int64_t D, int c,
+                     int w, double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+                     void* stream);
+int dca_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, void* o, float* lse, const int64_t* pos0,
+                            const int64_t* q_len, int64_t B, int64_t Lq, int64_t num_pages,
+                            int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv, int64_t D,
+                            int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
+                            size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -319,6 +319,76 @@ def decode_varlen(q, k_cache, v_cache, kv_len, c: int, w: int, base: float = 100
     return (o, lse) if return_lse else o
 
 
+def _check_pages(k_pages, v_pages, block_table, q):
+    _check(k_pages, "k_pages", 4, q.dtype)
+    _check(v_pages, "v_pages", 4, q.dtype)
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages differ in shape")
+    if (block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous()
+            or block_table.device != q.device):
+        raise ValueError("block_table must be a contiguous int32 [B, max_blocks] tensor on q's device")
+    return k_pages.shape[0], k_pages.shape[1], k_pages.shape[2], block_table.shape[1]
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_len, c: int, w: int, base: float = 10000.0,
+                 sm_scale: float | None = None, return_lse: bool = False, workspace=None):
+    """DCA decode over a paged cache: pools [num_pages, page_size, Hkv, D] (keys rotated
+    at j mod s), block_table int32 [B, max_blocks] on the device (row j of sequence b
+    at row j % page_size of page block_table[b, j // page_size]), kv_len per sequence.
+    page_size must be a multiple of 16."""
+    lib = _lib.load()
+    _check(q, "q", 3)
+    num_pages, page_size, Hkv, max_blocks = _check_pages(k_pages, v_pages, block_table, q)
+    B, Hq, D = q.shape
+    if k_pages.shape[3] != D or block_table.shape[0] != B:
+        raise ValueError("page pool / block table shapes do not match q")
+    code = _dtype_code(q)
+    kl, _ = _host_i64(kv_len, B, "kv_len")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(lib.dca_decode_varlen_workspace_bytes(kl, B, Hq, Hkv, D, code))
+    if nbytes == 0:
+        raise ValueError("invalid decode sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_decode_paged", lib.dca_decode_paged(
+        q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), o.data_ptr(), _ptr(lse),
+        kl, B, num_pages, page_size, max_blocks, Hq, Hkv, D, c, w, float(base), float(sm_scale or 0.0), code,
+        ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def prefill_chunk_paged(q, k_pages, v_pages, block_table, pos0, c: int, w: int, base: float = 10000.0,
+                        sm_scale: float | None = None, q_len=None, return_lse: bool = False, out=None,
+                        workspace=None):
+    """Chunked DCA prefill over a paged cache (layout as in decode_paged); otherwise as
+    prefill_chunk."""
+    lib = _lib.load()
+    _check(q, "q", 4)
+    num_pages, page_size, Hkv, max_blocks = _check_pages(k_pages, v_pages, block_table, q)
+    B, Lq, Hq, D = q.shape
+    if k_pages.shape[3] != D or block_table.shape[0] != B:
+        raise ValueError("page pool / block table shapes do not match q")
+    code = _dtype_code(q)
+    p0, p0v = _host_i64(pos0, B, "pos0")
+    if q_len is None:
+        ql, qlv = None, [Lq] * B
+    else:
+        ql, qlv = _host_i64(q_len, B, "q_len")
+    o = torch.zeros_like(q) if out is None else out
+    _check(o, "out", 4, q.dtype)
+    lse = torch.full((B, Hq, Lq), float("-inf"), dtype=torch.float32, device=q.device) if return_lse else None
+    max_keys = max(a + n for a, n in zip(p0v, qlv))
+    nbytes = int(lib.dca_prefill_workspace_bytes(B, max(max_keys, 1), Hkv, D, c, code))
+    if nbytes == 0:
+        raise ValueError("invalid chunked prefill sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check("dca_prefill_chunk_paged", lib.dca_prefill_chunk_paged(
+        q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), o.data_ptr(), _ptr(lse),
+        p0, ql, B, Lq, num_pages, page_size, max_blocks, Hq, Hkv, D, c, w, float(base),
+        float(sm_scale or 0.0), code, ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
 def coarse_fine_prefill(q, k, v, chunk: int, train_len: int, target_len: int, base: float = 10000.0,
                         sm_scale: float | None = None, return_lse: bool = False, workspace=None):
     """Causal prefill under the DCA guide's coarse / fine distance map (chunk size,

@@ -54,6 +54,10 @@ SIGNATURES = {
                                  _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _dbl,
                           _flt, _int, _vp, _sz, _vp]),
+    "dca_decode_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_prefill_chunk_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64,
+                                       _i64, _i64, _i64, _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -478,15 +478,23 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   return hip_status(launch_decode(a, dtype, (hipStream_t)stream));
 }
 
-int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                      const int64_t* pos0, const int64_t* q_len, int64_t B, int64_t Lq, int64_t cache_len,
-                      int64_t Hq, int64_t Hkv, int64_t D, int c, int w, double rope_base, float sm_scale,
-                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Chunked prefill over a dense cache (pg.bt null; cache_len rows per
+// sequence) or a paged one (cache_len = the most rows a sequence's table
+// covers).  Arguments are validated here.
+int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                       const int64_t* pos0, const int64_t* q_len, int64_t B, int64_t Lq, int64_t cache_len,
+                       int64_t Hq, int64_t Hkv, int64_t D, int c, int w, double rope_base, float sm_scale,
+                       int dtype, void* ws, size_t ws_bytes, void* stream, const PagedKv& pg) {
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!k_cache || !v_cache || !pos0 || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !base_ok(rope_base) || !cw_ok(c, w) || !attend_args_ok(q, o, lse, B, Lq, Hq, Hkv, sm_scale))
     return DCA_ERR_INVALID_ARG;
-  if (B < 1 || Lq < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || Lq > cache_len) return DCA_ERR_INVALID_ARG;
+  if (B < 1 || Lq < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || (!pg.bt && Lq > cache_len))
+    return DCA_ERR_INVALID_ARG;
   // per-sequence offsets and lengths (host memory, read here)
   int64_t max_keys = 0, rows = 0;
   for (int64_t b = 0; b < B; ++b) {
@@ -510,8 +518,10 @@ int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
     const int nb = (int)(B - b0 < kMaxSeqGroup ? B - b0 : kMaxSeqGroup);
     // copy the cached (already rotated) keys and the values into the tiles
     KvPrepArgs kp = {};
-    kp.k = (const uint8_t*)k_cache + b0 * kv_seq;
-    kp.v = (const uint8_t*)v_cache + b0 * kv_seq;
+    kp.k = (const uint8_t*)k_cache + (pg.bt ? 0 : b0 * kv_seq);
+    kp.v = (const uint8_t*)v_cache + (pg.bt ? 0 : b0 * kv_seq);
+    kp.pg = pg;
+    if (pg.bt) kp.pg.bt = pg.bt + b0 * pg.max_blocks;
     kp.table = nullptr;
     kp.krot = base + p.krot + b0 * ws_seq;
     kp.vt = dtype == DCA_BF16 ? base + p.vt + b0 * ws_seq : nullptr;
@@ -554,6 +564,7 @@ int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
     a.q_rows = (int)Lq;
     a.per_seq = 1;
     a.v_rows = (int)cache_len;
+    a.pg = kp.pg;
     a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
     const hipError_t e = dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st);
     if (e != hipSuccess) return DCA_ERR_HIP;
@@ -561,22 +572,12 @@ int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
   return DCA_OK;
 }
 
-size_t dca_decode_varlen_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
-                                         int64_t D, int dtype) {
-  if (!kv_len || B < 1 || B >= kMaxDim) return 0;
-  int64_t max_kv = 0;
-  for (int64_t b = 0; b < B; ++b) {
-    if (kv_len[b] < 1 || kv_len[b] >= kMaxDim / 2) return 0;
-    max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
-  }
-  DecodeLayout p;
-  return decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, &p) ? p.total : 0;
-}
-
-int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                      const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
-                      int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
-                      size_t ws_bytes, void* stream) {
+// Decode with per-sequence cache lengths over a dense cache (pg.bt null) or a
+// paged one (cache_len = the most rows a sequence's table covers).
+int decode_varlen_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                       const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
+                       int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
+                       size_t ws_bytes, void* stream, const PagedKv& pg) {
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !o || !kv_len) return DCA_ERR_INVALID_ARG;
   if (B < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || Hq < 1 || Hkv < 1 || Hq % Hkv)
@@ -599,8 +600,10 @@ int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, v
     const int nb = (int)(B - b0 < kMaxSeqGroup ? B - b0 : kMaxSeqGroup);
     DecodeArgs a = {};
     a.q = (const uint8_t*)q + b0 * Hq * D * es;
-    a.kc = (const uint8_t*)k_cache + b0 * cache_len * Hkv * D * es;
-    a.vc = (const uint8_t*)v_cache + b0 * cache_len * Hkv * D * es;
+    a.kc = (const uint8_t*)k_cache + (pg.bt ? 0 : b0 * cache_len * Hkv * D * es);
+    a.vc = (const uint8_t*)v_cache + (pg.bt ? 0 : b0 * cache_len * Hkv * D * es);
+    a.pg = pg;
+    if (pg.bt) a.pg.bt = pg.bt + b0 * pg.max_blocks;
     a.o = (uint8_t*)o + b0 * Hq * D * es;
     a.lse = lse ? lse + b0 * Hq : nullptr;
     a.qv = base + p.qv + b0 * Hq * 3 * D * es;
@@ -625,6 +628,77 @@ int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, v
     if (e != hipSuccess) return DCA_ERR_HIP;
   }
   return DCA_OK;
+}
+
+// Paged-cache arguments: pool sizes and the block table (device memory, not
+// read on the host).  page_size must be a multiple of 16.
+bool paged_ok(const int32_t* block_table, int64_t B, int64_t num_pages, int64_t page_size, int64_t max_blocks,
+              PagedKv* pg) {
+  if (!block_table || !aligned(block_table, 4)) return false;
+  if (num_pages < 1 || num_pages >= kMaxDim || page_size < 16 || page_size % 16 || page_size >= kMaxDim / 2)
+    return false;
+  if (max_blocks < 1 || max_blocks >= kMaxDim || B * max_blocks >= kMaxDim) return false;
+  if (max_blocks * page_size >= kMaxDim / 2) return false;
+  pg->bt = block_table;
+  pg->page_size = (int)page_size;
+  pg->max_blocks = (int)max_blocks;
+  pg->num_pages = (int)num_pages;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dca_decode_varlen_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
+                                         int64_t D, int dtype) {
+  if (!kv_len || B < 1 || B >= kMaxDim) return 0;
+  int64_t max_kv = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    if (kv_len[b] < 1 || kv_len[b] >= kMaxDim / 2) return 0;
+    max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
+  }
+  DecodeLayout p;
+  return decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+}
+
+int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int64_t* pos0, const int64_t* q_len, int64_t B, int64_t Lq, int64_t cache_len,
+                      int64_t Hq, int64_t Hkv, int64_t D, int c, int w, double rope_base, float sm_scale,
+                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_chunk_impl(q, k_cache, v_cache, o, lse, pos0, q_len, B, Lq, cache_len, Hq, Hkv, D, c, w,
+                            rope_base, sm_scale, dtype, ws, ws_bytes, stream, PagedKv{});
+}
+
+int dca_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
+                      int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return decode_varlen_impl(q, k_cache, v_cache, o, lse, kv_len, B, cache_len, Hq, Hkv, D, c, w, rope_base,
+                            sm_scale, dtype, ws, ws_bytes, stream, PagedKv{});
+}
+
+int dca_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                            void* o, float* lse, const int64_t* pos0, const int64_t* q_len, int64_t B, int64_t Lq,
+                            int64_t num_pages, int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv,
+                            int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  PagedKv pg;
+  if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
+  return prefill_chunk_impl(q, k_pages, v_pages, o, lse, pos0, q_len, B, Lq, max_blocks * page_size, Hq, Hkv,
+                            D, c, w, rope_base, sm_scale, dtype, ws, ws_bytes, stream, pg);
+}
+
+int dca_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,
+                     float* lse, const int64_t* kv_len, int64_t B, int64_t num_pages, int64_t page_size,
+                     int64_t max_blocks, int64_t Hq, int64_t Hkv, int64_t D, int c, int w, double rope_base,
+                     float sm_scale, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  PagedKv pg;
+  if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
+  return decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, max_blocks * page_size, Hq, Hkv, D, c, w,
+                            rope_base, sm_scale, dtype, ws, ws_bytes, stream, pg);
 }
 
 }  // extern "C"

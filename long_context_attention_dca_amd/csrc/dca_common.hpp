@@ -165,4 +165,14 @@ struct Elem<uint16_t> {
   __device__ static void store(uint16_t* p, float x) { *p = f2bf(x); }
 };
 
+// Cache row of key j of sequence b: dense [B, rows, ...] or paged (the row
+// inside the page pool).  -1 when the block-table entry lies outside the pool;
+// callers then read nothing and poison what they produce with NaN.
+template <typename PG>
+__device__ inline int64_t cache_row(const PG& pg, int64_t dense_rows, int b, int j) {
+  if (!pg.bt) return (int64_t)b * dense_rows + j;
+  const int page = pg.bt[(int64_t)b * pg.max_blocks + j / pg.page_size];
+  return (page >= 0 && page < pg.num_pages) ? (int64_t)page * pg.page_size + j % pg.page_size : -1;
+}
+
 }  // namespace dca

@@ -31,6 +31,14 @@ hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int
 // copied as they are.  For bf16 with vt non-null, also the tiled,
 // key-permuted V transpose vt [B, Hkv, Lp/64, D, 64].  Rows at or past a
 // sequence's valid length are written as zeros.
+// A paged KV cache: k / v point at page pools [num_pages, page_size, Hkv, D];
+// row j of sequence b is row j mod page_size of page bt[b * max_blocks +
+// j / page_size].  bt null: the dense layout.
+struct PagedKv {
+  const int* bt;
+  int page_size, max_blocks, num_pages;
+};
+
 struct KvPrepArgs {
   const void* k;        // [B, in_rows, Hkv, D]
   const void* v;        // [B, in_rows, Hkv, D]
@@ -48,6 +56,7 @@ struct KvPrepArgs {
   int cf_chunk;
   double cf_step;
   const double* theta;  // pos_mode 1: theta_k table [D/2]
+  PagedKv pg;           // paged k / v (in_rows unused), or bt null
 };
 hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st);
 
@@ -89,6 +98,7 @@ struct PrefillArgs {
   // kMapCoarseFine: 1 / kappa = L_train / L_target.
   double cf_inv_kappa;
   const double* theta;  // theta_k table [D/2] for the fp64 rotations of real positions
+  PagedKv pg;           // fp32 kernels: raw V in a paged pool (v_rows unused), or bt null
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
@@ -118,6 +128,7 @@ struct DecodeArgs {
   // key range) items; sequence b's waves start at wave_start[b] (set by the
   // launcher).
   int wave_start[kMaxSeqGroup + 1];
+  PagedKv pg;          // kc / vc are page pools (cache_len unused), or bt null
 };
 
 // Split plan shared by the workspace queries and the launchers: kv holds the

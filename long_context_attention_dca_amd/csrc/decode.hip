@@ -71,7 +71,9 @@ __global__ void decode_qprep_kernel(DecodeArgs a) {
 }
 
 // ---- 2. split kernel, bf16 MFMA ----------------------------------------------------
-template <int D>
+// PAGED: the caches are page pools (a.pg); the dense instantiation carries
+// none of the block-table work.
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   constexpr int NDS = D / 16;
@@ -120,9 +122,9 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
 
   uint8_t* kl = smem + wave * WBYTES;
   uint8_t* vl = kl + KBYTES;
-  const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive keys
-  const uint16_t* kc = (const uint16_t*)a.kc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
-  const uint16_t* vc = (const uint16_t*)a.vc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
+  const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive cache rows
+  const uint16_t* kc = (const uint16_t*)a.kc + (int64_t)g * D;
+  const uint16_t* vc = (const uint16_t*)a.vc + (int64_t)g * D;
   const uint16_t* qv = (const uint16_t*)a.qv + ((int64_t)b * a.Hq + hq) * 3 * D;
 
   bf16x8 qf[NDS];
@@ -134,23 +136,57 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
     }
   };
 
+  // Cache rows of keys j0 + 16 h .. j0 + 16 h + 15 (h = 0, 1) are
+  // consecutive in both layouts: j0 is a multiple of 32 and a page holds a
+  // multiple of 16 rows.  Paged: one (scalar) block-table read per half.
+  int64_t rb[2] = {0, 0};
+  bool bad = false;   // a block-table entry outside the pool: output NaN
+  auto rows_of = [&](int j0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = j0 + 16 * h;
+      if constexpr (PAGED) {
+        // b and j are wave-uniform, so is the page: keep it in scalar registers
+        int page = j < kend ? a.pg.bt[(int64_t)b * a.pg.max_blocks + j / a.pg.page_size] : 0;
+        page = __builtin_amdgcn_readfirstlane(page);
+        const bool ok = page >= 0 && page < a.pg.num_pages;
+        bad |= !ok;
+        rb[h] = ok ? (int64_t)page * a.pg.page_size + j % a.pg.page_size : 0;
+      } else {
+        rb[h] = (int64_t)b * a.cache_len + j;
+      }
+    }
+  };
+  // Byte address of a load = (wave-uniform base: the half's first cache row
+  // plus the first row of the load instruction) + (one 32-bit lane offset,
+  // the same for every load).
+  const uint32_t rs2 = (uint32_t)(row_stride * 2);
+  const uint32_t lane_off = (uint32_t)(lane / CPR) * rs2 + (uint32_t)(lane % CPR) * 16;
+  // lo: lane_off made opaque once per sub-tile, so that the compiler cannot
+  // hoist 64-bit per-load addresses out of the key loop (they would not fit
+  // in registers next to the accumulators).
+  auto paddr = [&](const uint16_t* base, int it, uint32_t lo) __attribute__((always_inline)) {
+    const int r0 = it * 64 / CPR;   // first row of load instruction it
+    const char* sb = (const char*)(base + rb[r0 >> 4] * row_stride) + (size_t)(r0 & 15) * rs2;
+    return (const uint4*)(sb + lo);
+  };
   uint4 kreg[NI], vreg[NI];
   auto gload_k = [&](int j0) {
+    uint32_t lo = lane_off;
+    asm volatile("" : "+v"(lo));
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const int id = it * 64 + lane;
-      const int row = id / CPR, ch = id % CPR;
-      const int j = j0 + row;
-      kreg[it] = (j < kend) ? *(const uint4*)(kc + (int64_t)j * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
+      const int j = j0 + (it * 64 + lane) / CPR;
+      kreg[it] = (j < kend) ? *paddr(kc, it, lo) : make_uint4(0, 0, 0, 0);
     }
   };
   auto gload_v = [&](int j0) {
+    uint32_t lo = lane_off;
+    asm volatile("" : "+v"(lo));
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const int id = it * 64 + lane;
-      const int row = id / CPR, ch = id % CPR;
-      const int j = j0 + row;
-      vreg[it] = (j < kend) ? *(const uint4*)(vc + (int64_t)j * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
+      const int j = j0 + (it * 64 + lane) / CPR;
+      vreg[it] = (j < kend) ? *paddr(vc, it, lo) : make_uint4(0, 0, 0, 0);
     }
   };
   auto lstore_k = [&]() {
@@ -191,6 +227,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   float m_run = kNoMax, l_run = 0.f;
   int cur_cls = -1;
 
+  rows_of(kbeg);
   gload_k(kbeg);
   gload_v(kbeg);
   for (int j0 = kbeg; j0 < kend; j0 += SUB) {
@@ -199,7 +236,10 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
     // other half's loads stay in flight meanwhile.
     const bool more = j0 + SUB < kend;
     lstore_k();
-    if (more) gload_k(j0 + SUB);
+    if (more) {
+      rows_of(j0 + SUB);
+      gload_k(j0 + SUB);
+    }
     lstore_v();
     if (more) gload_v(j0 + SUB);
     __builtin_amdgcn_wave_barrier();
@@ -287,7 +327,8 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   if (qvalid) {
     const int64_t pidx = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
     float* po = a.part_o + pidx * D;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // empty range: O 0, LSE -inf
+    // empty range: O 0, LSE -inf; an unreadable page: NaN
+    const float inv = (PAGED && bad) ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -296,7 +337,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
                                 oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv);
         *(float4*)(po + db * 32 + grp * 8 + hh * 4) = o4;
       }
-    if (hh == 0) a.part_lse[pidx] = m_run + log2f(l_tot);
+    if (hh == 0) a.part_lse[pidx] = (PAGED && bad) ? __builtin_nanf("") : m_run + log2f(l_tot);
   }
 }
 
@@ -318,19 +359,26 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
   const float* qv = (const float*)a.qv + (int64_t)bh * 3 * D;
   for (int idx = tid; idx < 3 * D; idx += 256) qs[idx / D][idx % D] = qv[idx];
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const float* kc = (const float*)a.kc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
-  const float* vc = (const float*)a.vc + ((int64_t)b * a.cache_len * a.Hkv + g) * D;
+  const float* kc = (const float*)a.kc + (int64_t)g * D;
+  const float* vc = (const float*)a.vc + (int64_t)g * D;
+  __shared__ int64_t rows[256];   // cache row of each key of the current step (-1: unreadable page)
   float m = -INFINITY, l = 0.f, o = 0.f;  // thread tid < D owns output dim tid
   __syncthreads();
   for (int jb = kbeg; jb < kend; jb += 256) {
     const int j = jb + tid;
     float x = -INFINITY;
     if (j < kend) {
-      const int cls = min(nq - j / s, 2);
-      const float* kr = kc + (int64_t)j * row_stride;
-      float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc = fmaf(qs[cls][d], kr[d], acc);
-      x = acc * a.sm_scale;
+      const int64_t row = cache_row(a.pg, a.cache_len, b, j);
+      rows[tid] = row;
+      if (row < 0) {
+        x = __builtin_nanf("");   // unreadable page: the row's result becomes NaN
+      } else {
+        const int cls = min(nq - j / s, 2);
+        const float* kr = kc + row * row_stride;
+        float acc = 0.f;
+        for (int d = 0; d < D; ++d) acc = fmaf(qs[cls][d], kr[d], acc);
+        x = acc * a.sm_scale;
+      }
     }
     float mx = x;
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -351,7 +399,8 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
     if (tid < D) {
       float acc = o * alpha;
       const int nk = min(256, kend - jb);
-      for (int t = 0; t < nk; ++t) acc = fmaf(sc[t], vc[(int64_t)(jb + t) * row_stride + tid], acc);
+      for (int t = 0; t < nk; ++t)
+        acc = fmaf(sc[t], rows[t] < 0 ? 0.f : vc[rows[t] * row_stride + tid], acc);
       o = acc;
     }
     __syncthreads();
@@ -468,10 +517,18 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
     }
     const dim3 grid((unsigned)((waves + 3) / 4));
     const float scale_log2 = a.sm_scale * kLog2e;
-    if (a.D == 64)
-      hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, dim3(256), 0, st, b, nqg, scale_log2);
-    else
-      hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, dim3(256), 0, st, b, nqg, scale_log2);
+    const bool paged = a.pg.bt != nullptr;
+    if (a.D == 64) {
+      if (paged)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      else
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+    } else {
+      if (paged)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      else
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+    }
     hipLaunchKernelGGL(decode_combine_kernel<uint16_t>, dim3(nbh), dim3(128), 0, st, a);
   }
   return hipGetLastError();

@@ -888,7 +888,8 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
       const int j = j0 + row;
       ks[row][d] = krot[(int64_t)j * D + d];
       if constexpr (MAP != kMapDCA) ks2[row][d] = krot2[(int64_t)j * D + d];
-      vs[row][d] = (j < L) ? vraw[(((int64_t)b * a.v_rows + j) * a.Hkv + g) * D + d] : 0.f;
+      const int64_t crow = j < L ? cache_row(a.pg, a.v_rows, b, j) : 0;
+      vs[row][d] = j >= L ? 0.f : (crow < 0 ? __builtin_nanf("") : vraw[(crow * a.Hkv + g) * D + d]);
     }
     __syncthreads();
     float sc[2];

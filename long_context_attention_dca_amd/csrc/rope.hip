@@ -133,8 +133,12 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
     const int row = idx / half, kk = idx - row * half;
     const int j = j0 + row;
     T* dst = krot + (bg * a.Lp + j) * D;
-    if (j < Lb) {
-      const int64_t in = (((int64_t)b * a.in_rows + j) * a.Hkv + g) * D;
+    const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : 0;
+    if (j < Lb && crow < 0) {   // unreadable page: poison the key so the rows using it give NaN
+      Elem<T>::store(dst + kk, __builtin_nanf(""));
+      Elem<T>::store(dst + kk + half, __builtin_nanf(""));
+    } else if (j < Lb) {
+      const int64_t in = (crow * a.Hkv + g) * D;
       const double x1 = Elem<T>::load(k + in + kk);
       const double x2 = Elem<T>::load(k + in + kk + half);
       if (a.table || a.pos_mode == 1) {
@@ -166,7 +170,8 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
     for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
       const int row = idx / D, d = idx - row * D;
       const int j = j0 + row;
-      vs[row][d] = (j < Lb) ? vv[(((int64_t)b * a.in_rows + j) * a.Hkv + g) * D + d] : (uint16_t)0;
+      const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : -1;
+      vs[row][d] = crow >= 0 ? vv[(crow * a.Hkv + g) * D + d] : (uint16_t)0;
     }
     __syncthreads();
     const int ntiles = a.Lp / TK;

@@ -283,3 +283,38 @@ def test_coarse_fine_workspace_and_validation(lib):
         a = list(ok)
         a[i] = bad
         assert lib.dca_coarse_fine_prefill(*a) == st, (i, bad)
+
+
+def test_decode_paged_validation(lib):
+    # q, k_pages, v_pages, block_table, o, lse, kv_len, B, num_pages, page_size, max_blocks, Hq, Hkv, D,
+    # c, w, base, sm_scale, dtype, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(40, 100), 2, 20, 16, 8, 8, 2, 64, 128, 32, 1e4, 0.0, 1,
+          FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(3, None, -1),            # no block table
+                       (9, 8, -1), (9, 24, -1), (9, 0, -1),   # page size not a multiple of 16
+                       (8, 0, -1), (10, 0, -1),  # empty pool / table
+                       (6, _i64s(40, 129), -1),  # 129 rows > 8 blocks of 16
+                       (6, _i64s(0, 5), -1),
+                       (13, 96, -2), (18, 3, -2),
+                       (20, 64, -3), (19, None, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_decode_paged(*a) == st, (i, bad)
+
+
+def test_prefill_chunk_paged_validation(lib):
+    # q, k_pages, v_pages, block_table, o, lse, pos0, q_len, B, Lq, num_pages, page_size, max_blocks,
+    # Hq, Hkv, D, c, w, base, sm_scale, dtype, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(32, 64), None, 2, 32, 20, 32, 4, 8, 2, 128, 256, 64, 1e4,
+          0.0, 1, FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(3, None, -1), (11, 17, -1), (12, 0, -1),
+                       (6, _i64s(32, 97), -1),   # 97 + 32 rows > 4 blocks of 32
+                       (6, _i64s(-1, 0), -1),
+                       (15, 80, -2), (22, 64, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_prefill_chunk_paged(*a) == st, (i, bad)
+    # no rows at all: nothing to do, no device call
+    a = list(ok)
+    a[7] = _i64s(0, 0)
+    assert lib.dca_prefill_chunk_paged(*a) == 0
