@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-selfextend", action="store_true", help="skip the SelfExtend 32k prefill")
     ap.add_argument("--no-chunked", action="store_true",
-                    help="skip the chunked 32k prefill and the ragged 100k decode")
+                    help="skip the chunked 32k prefill and the ragged / paged 100k decodes")
     ap.add_argument("--no-coarse-fine", action="store_true", help="skip the coarse / fine map 32k prefill")
     ap.add_argument("--only", choices=["prefill", "decode", "prefill128k", "selfextend", "coarsefine"], default=None,
                     help="run one workload only (for profiling)")
@@ -298,6 +298,36 @@ def main():
         result["decode_varlen_100k"] = {"ms": dv_ms, "achieved": nbv / (dv_ms * 1e-3) / 1e9, "unit": "GB/s",
                                         "frac": nbv / (dv_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                                         "kv_len": f"{kvr[0]}..{kvr[-1]} evenly spaced", "bytes_per_call": nbv}
+        # the same ragged batch from a paged cache: pages of 16 rows handed out
+        # in a seeded random order (the pools are built untimed)
+        PG = 16
+        nblk = -(-DC["kv_len"] // PG)
+        perm = torch.randperm(DC["B"] * nblk, generator=torch.Generator().manual_seed(DC["seed"])).to(dev)
+        table = perm.view(DC["B"], nblk).to(torch.int32).contiguous()
+        pools = []
+        for x in (kc, vc):
+            pool = torch.empty(DC["B"] * nblk, PG, DC["Hkv"], DC["D"], dtype=x.dtype, device=dev)
+            padded = torch.zeros(DC["B"], nblk * PG, DC["Hkv"], DC["D"], dtype=x.dtype, device=dev)
+            padded[:, : DC["kv_len"]] = x
+            pool[perm] = padded.view(DC["B"] * nblk, PG, DC["Hkv"], DC["D"])
+            del padded
+            pools.append(pool)
+        paged_call = lambda: dca.decode_paged(dq, pools[0], pools[1], table, kvr, DC["c"], DC["w"], DC["base"],
+                                              workspace=dvws)
+        paged_call()
+        torch.cuda.synchronize()
+        pv = [events(2) for _ in range(nd)]
+        for i in range(nd):
+            pv[i][0].record()
+            paged_call()
+            pv[i][1].record()
+        torch.cuda.synchronize()
+        pg_ms = sum(e[0].elapsed_time(e[1]) for e in pv) / nd
+        result["decode_paged_100k"] = {"ms": pg_ms, "achieved": nbv / (pg_ms * 1e-3) / 1e9, "unit": "GB/s",
+                                       "frac": nbv / (pg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "page_size": PG,
+                                       "kv_len": f"{kvr[0]}..{kvr[-1]} evenly spaced", "bytes_per_call": nbv}
+        del pools, table, perm
+        torch.cuda.empty_cache()
 
     # ---------------- SelfExtend 32k prefill (reported beside the step) ---------
     if run_se:
