@@ -178,8 +178,9 @@ int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L,
  *   queries at i, i - o_i (1 - 1/kappa) or c_i C / kappa + o_i.
  * These positions and their cos / sin are evaluated in fp64.
  *
- * dca_coarse_fine_workspace_bytes: scratch for the fp64 theta table, the two
- * key rotations and the V layout (0 on invalid sizes).
+ * dca_coarse_fine_workspace_bytes: scratch for the fp64 theta table, the fp64
+ * (cos, sin) of the three query positions of every row (3 * L * D/2 * 16
+ * bytes), the two key rotations and the V layout (0 on invalid sizes).
  * dca_coarse_fine_prefill: q [B, L, Hq, D], k / v [B, L, Hkv, D] raw; o, lse,
  *   sm_scale, GQA, dtypes as in dca_prefill.  chunk >= 1, train_len >= 1,
  *   target_len >= 1.  bf16 needs chunk to be a multiple of 64, so that every

@@ -335,27 +335,33 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }
 
-// Coarse / fine map workspace: theta_k table (512 B) | keys at their plain
+// Coarse / fine map workspace: theta_k table (512 B) | (cos, sin) of the three
+// query positions of every row, [3][L][D/2] double2 | keys at their plain
 // positions | keys at the coarse-scaled positions | V (bf16: tiled transpose;
 // fp32: unused).
 constexpr size_t kThetaBytes = 512;   // D/2 <= 64 doubles
 
-static bool cf_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype, int64_t* Lp, size_t* krot2,
-                      size_t* vt, size_t* total) {
+struct CfLayout {
+  int64_t Lp;
+  size_t qtab, krot, krot2, vt, total;
+};
+
+static bool cf_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype, CfLayout* p) {
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype)) return false;
   if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
-  *Lp = round_up(L, kPrefillTileKeys);
-  const int64_t kbytes = round_up(B * Hkv * *Lp * D * elem_size(dtype), 256);
-  *krot2 = kThetaBytes + (size_t)kbytes;
-  *vt = kThetaBytes + (size_t)(2 * kbytes);
-  *total = kThetaBytes + (size_t)(3 * kbytes);
+  p->Lp = round_up(L, kPrefillTileKeys);
+  const int64_t kbytes = round_up(B * Hkv * p->Lp * D * elem_size(dtype), 256);
+  p->qtab = kThetaBytes;
+  p->krot = p->qtab + (size_t)round_up(3 * L * (D / 2) * 16, 256);
+  p->krot2 = p->krot + (size_t)kbytes;
+  p->vt = p->krot2 + (size_t)kbytes;
+  p->total = p->vt + (size_t)kbytes;
   return true;
 }
 
 size_t dca_coarse_fine_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype) {
-  int64_t Lp;
-  size_t k2, vt, total;
-  return cf_layout(B, L, Hkv, D, dtype, &Lp, &k2, &vt, &total) ? total : 0;
+  CfLayout p;
+  return cf_layout(B, L, Hkv, D, dtype, &p) ? p.total : 0;
 }
 
 int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -369,26 +375,27 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
   if (chunk < 1 || chunk > (1 << 24) || train_len < 1 || target_len < 1) return DCA_ERR_INVALID_ARG;
   // bf16 runs the two-group kernel: every 32-row block and 64-key tile inside one chunk
   if (dtype == DCA_BF16 && chunk % kPrefillTileKeys != 0) return DCA_ERR_UNSUPPORTED;
-  int64_t Lp;
-  size_t off_k2, off_vt, total;
-  if (!cf_layout(B, L, Hkv, D, dtype, &Lp, &off_k2, &off_vt, &total)) return DCA_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
+  CfLayout p;
+  if (!cf_layout(B, L, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
   const double inv_kappa = (double)train_len / (double)target_len;
   double* theta = (double*)base;
   if (launch_rope_theta(theta, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  double2* qtab = (double2*)(base + p.qtab);
+  if (launch_cf_query_table(qtab, (int)L, (int)D, chunk, inv_kappa, theta, st) != hipSuccess) return DCA_ERR_HIP;
   // keys at plain positions (with the V layout), then at coarse-scaled positions
   KvPrepArgs kp = {};
   kp.k = k;
   kp.v = v;
   kp.table = nullptr;
-  kp.krot = base + kThetaBytes;
-  kp.vt = dtype == DCA_BF16 ? base + off_vt : nullptr;
+  kp.krot = base + p.krot;
+  kp.vt = dtype == DCA_BF16 ? base + p.vt : nullptr;
   kp.B = (int)B;
   kp.in_rows = (int)L;
   kp.L = (int)L;
-  kp.Lp = (int)Lp;
+  kp.Lp = (int)p.Lp;
   kp.Hkv = (int)Hkv;
   kp.D = (int)D;
   kp.kdiv = 1;
@@ -398,21 +405,21 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
   kp.cf_step = (double)chunk;
   kp.theta = theta;
   if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
-  kp.krot = base + off_k2;
+  kp.krot = base + p.krot2;
   kp.vt = nullptr;
   kp.cf_step = (double)chunk * inv_kappa;
   if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
   PrefillArgs a = {};
   a.q = q;
-  a.krot = base + kThetaBytes;
-  a.krot2 = base + off_k2;
-  a.vt = dtype == DCA_BF16 ? (const void*)(base + off_vt) : v;   // fp32 reads V as given
-  a.table = nullptr;
+  a.krot = base + p.krot;
+  a.krot2 = base + p.krot2;
+  a.vt = dtype == DCA_BF16 ? (const void*)(base + p.vt) : v;   // fp32 reads V as given
+  a.table = qtab;
   a.o = o;
   a.lse = lse;
   a.B = (int)B;
   a.L = (int)L;
-  a.Lp = (int)Lp;
+  a.Lp = (int)p.Lp;
   a.Hq = (int)Hq;
   a.Hkv = (int)Hkv;
   a.D = (int)D;
@@ -424,8 +431,6 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
   a.q_rows = (int)L;
   a.per_seq = 0;
   a.v_rows = (int)L;
-  a.cf_inv_kappa = inv_kappa;
-  a.theta = theta;
   a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
   return hip_status(dtype == DCA_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st));
 }

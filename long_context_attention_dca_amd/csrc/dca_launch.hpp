@@ -18,6 +18,10 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipStream_t st);
 // theta_k = base^(-2k/D) for k < D/2, fp64 (for real-valued positions).
 hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st);
+// Coarse / fine map: (cos, sin) of the three query positions of rows 0 .. L-1,
+// [3][L][D/2] double2, from theta (chunk C, 1 / kappa = inv_kappa).
+hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
+                                 hipStream_t st);
 
 // dca_rope_remap kernel (dtype 0 = fp32, 1 = bf16).
 hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
@@ -78,7 +82,8 @@ struct PrefillArgs {
   const void* krot;    // [B, Hkv, Lp, D] rotated keys (DCA: at j mod s; SelfExtend: at j)
   const void* krot2;   // SelfExtend only: keys at floor(j / G); null for DCA
   const void* vt;      // bf16: [B, Hkv, Lp/64, D, 64]; fp32: raw v [B, L, Hkv, D]
-  const double2* table; // [npos, D/2] (cos, sin) in fp64
+  const double2* table; // [npos, D/2] (cos, sin) in fp64; kMapCoarseFine: [3][L][D/2],
+                        // the intra / successive / inter query positions of every row
   void* o;             // [B, L, Hq, D]
   float* lse;          // [B, Hq, L] or null
   int B, L, Lp, Hq, Hkv, D, c, w, s;
@@ -95,9 +100,6 @@ struct PrefillArgs {
   int seq_q0[kMaxSeqGroup];
   int seq_len[kMaxSeqGroup];
   int v_rows;          // fp32 kernels: rows per sequence of the raw V in vt
-  // kMapCoarseFine: 1 / kappa = L_train / L_target.
-  double cf_inv_kappa;
-  const double* theta;  // theta_k table [D/2] for the fp64 rotations of real positions
   PagedKv pg;           // fp32 kernels: raw V in a paged pool (v_rows unused), or bt null
 };
 

@@ -491,15 +491,16 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 
   bf16x8 qf[NDS];
   auto load_q = [&](int cls) __attribute__((always_inline)) {
-    int P = 0;
-    double Pf = 0.0;   // coarse / fine map: a real position, cos/sin made in fp64
-    if constexpr (MAP == kMapSelfExtend)
-      P = cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window);
-    else if constexpr (MAP == kMapCoarseFine)
-      Pf = cf_query_pos(cls, qrow, c, a.cf_inv_kappa);
-    else
-      P = query_pos(cls, rq, s, c);
-    const double2* tb = a.table + (int64_t)P * (D / 2);   // read only for rows < L
+    // this row's (cos, sin) row of the table, read only for rows < L
+    const double2* tb;
+    if constexpr (MAP == kMapCoarseFine) {   // real positions: one table row per (variant, row)
+      tb = a.table + ((int64_t)cls * a.L + qrow) * (D / 2);
+    } else {
+      const int P = MAP == kMapSelfExtend
+                        ? (cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window))
+                        : query_pos(cls, rq, s, c);
+      tb = a.table + (int64_t)P * (D / 2);
+    }
     if (qrow < L) {
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds) {
@@ -510,11 +511,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         unpack_bf16x8(u2, x2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          double2 t;
-          if constexpr (MAP == kMapCoarseFine)
-            t = rope_cs(Pf, a.theta[ds * 16 + hh * 8 + e]);
-          else
-            t = tb[ds * 16 + hh * 8 + e];
+          const double2 t = tb[ds * 16 + hh * 8 + e];
           y1[e] = (float)((double)x1[e] * t.x - (double)x2[e] * t.y);
           y2[e] = (float)((double)x2[e] * t.x + (double)x1[e] * t.y);
         }
@@ -861,7 +858,7 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
     for (int cls = 0; cls < NV; ++cls) {
       double2 t;
       if constexpr (MAP == kMapCoarseFine) {
-        t = rope_cs(cf_query_pos(cls, ii, c, a.cf_inv_kappa), a.theta[k]);
+        t = a.table[((int64_t)cls * a.L + ii) * HALF + k];
       } else {
         int P;
         if constexpr (MAP == kMapSelfExtend)

@@ -41,6 +41,18 @@ hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st) 
   return hipGetLastError();
 }
 
+__global__ void cf_query_table_kernel(double2* __restrict__ tab, int L, int half, int C, double inv_kappa,
+                                      const double* __restrict__ theta) {
+  const int i = blockIdx.x, cls = blockIdx.y, k = threadIdx.x;
+  if (k < half) tab[((int64_t)cls * L + i) * half + k] = rope_cs(cf_query_pos(cls, i, C, inv_kappa), theta[k]);
+}
+
+hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(cf_query_table_kernel, dim3(L, 3), dim3(64), 0, st, tab, L, D / 2, C, inv_kappa, theta);
+  return hipGetLastError();
+}
+
 // ---- dca_rope_remap -----------------------------------------------------------------
 // One workgroup per token t: the 64 (or 32) angles of its position are made
 // once in fp64 and applied to every (batch, head) row of that token.

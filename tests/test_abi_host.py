@@ -275,7 +275,8 @@ def test_decode_varlen_workspace_sizes(lib):
 def test_coarse_fine_workspace_and_validation(lib):
     Lp = 128
     kbytes = 2 * 3 * Lp * 128 * 2
-    assert lib.dca_coarse_fine_workspace_bytes(2, 100, 3, 128, 1) == 512 + 3 * kbytes   # theta table first
+    # theta table, then the (cos, sin) of the 3 query positions of 100 rows, then keys twice and V
+    assert lib.dca_coarse_fine_workspace_bytes(2, 100, 3, 128, 1) == 512 + 3 * 100 * 64 * 16 + 3 * kbytes
     assert lib.dca_coarse_fine_workspace_bytes(2, 100, 3, 96, 1) == 0
     ok = [FAKE, FAKE, FAKE, FAKE, None, 1, 256, 4, 2, 128, 512, 4096, 32768, 1e4, 0.0, 1, FAKE_WS, 1 << 30, None]
     for i, bad, st in [(0, None, -1), (10, 0, -1), (11, 0, -1), (12, -5, -1), (10, 96, -2), (9, 80, -2),
