@@ -102,7 +102,7 @@ int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, in
 /*
  * Scratch bytes dca_prefill needs for these sizes (0 on invalid sizes).
  * Holds the fp64 rope cos/sin table [c, D/2], the rotated keys (head-major,
- * padded to a multiple of 64 rows) and the values (bf16: tiled transpose;
+ * padded to a multiple of 128 rows) and the values (bf16: tiled transpose;
  * fp32: a copy).
  */
 size_t dca_prefill_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c,
@@ -143,7 +143,7 @@ int dca_prefill(const void* q, const void* k, const void* v, void* o, float* lse
  *
  * dca_prefill_prepare: builds, inside ws, the fp64 cos/sin table for positions
  * [0, c), the keys rotated at j mod s (head-major, rows padded to a multiple
- * of 64) and the value layout the attention kernel reads (bf16: a tiled
+ * of 128) and the value layout the attention kernel reads (bf16: a tiled
  * transpose; fp32: a copy).  k_rot_out as in dca_prefill (may be NULL).
  *
  * dca_prefill_attend: the fused attention kernel over a workspace prepared by
@@ -248,7 +248,7 @@ int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
  *
  * dca_selfextend_workspace_bytes: scratch bytes for these sizes (0 on invalid
  * sizes): the fp64 cos/sin table for every position used, the keys rotated at
- * j and at floor(j/G) (head-major, rows padded to a multiple of 64) and the
+ * j and at floor(j/G) (head-major, rows padded to a multiple of 128) and the
  * value layout (bf16: tiled transpose; fp32: a copy).
  *
  * dca_selfextend_prefill:

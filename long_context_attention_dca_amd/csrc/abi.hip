@@ -33,7 +33,7 @@ bool prefill_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c, int dty
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype) || c < 1) return false;
   if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
   PrefillLayout p;
-  p.Lp = round_up(L, kPrefillTileKeys);
+  p.Lp = round_up(L, kPrefillRowAlign);
   const int64_t tbytes = (int64_t)c * (D / 2) * 16;
   const int64_t kbytes = B * Hkv * p.Lp * D * elem_size(dtype);
   const int64_t vbytes = B * Hkv * p.Lp * D * elem_size(dtype);
@@ -58,7 +58,7 @@ bool se_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int G, int W, int d
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype) || !se_ok(G, W)) return false;
   if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
   SeLayout p;
-  p.Lp = round_up(L, kPrefillTileKeys);
+  p.Lp = round_up(L, kPrefillRowAlign);
   // largest position used: L - 1 (neighbor query) or the grouped query of row L - 1
   const int64_t top_grouped = (L - 1) / G + W - W / G;
   p.npos = (top_grouped > L - 1 ? top_grouped : L - 1) + 1;
@@ -349,7 +349,7 @@ struct CfLayout {
 static bool cf_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype, CfLayout* p) {
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype)) return false;
   if (B >= kMaxDim || L >= kMaxDim / 2 || Hkv >= kMaxDim) return false;
-  p->Lp = round_up(L, kPrefillTileKeys);
+  p->Lp = round_up(L, kPrefillRowAlign);
   const int64_t kbytes = round_up(B * Hkv * p->Lp * D * elem_size(dtype), 256);
   p->qtab = kThetaBytes;
   p->krot = p->qtab + (size_t)round_up(3 * L * (D / 2) * 16, 256);

@@ -7,7 +7,8 @@
 
 namespace dca {
 
-constexpr int kPrefillTileKeys = 64;  // key rows per prefill K/V tile
+constexpr int kPrefillTileKeys = 64;  // keys per V tile of the prefill layout (and per prepare block)
+constexpr int kPrefillRowAlign = 128; // key rows per head are padded to this (the widest key tile)
 // Sequences whose own lengths / offsets one launch carries in its kernel
 // arguments (ragged batches are launched in groups of at most this many).
 constexpr int kMaxSeqGroup = 64;

@@ -346,19 +346,21 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 }
 
 // ---- bf16 ping-pong kernel (chunk size a multiple of 64) ------------------------
-// One workgroup = 8 waves = 256 query rows of one head.  Waves 0-3 (group 0)
-// and 4-7 (group 1) share the four SIMDs one-to-one and alternate, phase by
-// phase, between
-//   X(t): O^T += V(t-1)^T P(t-1)^T, then S^T(t) = K(t) Q^T    (32 MFMAs)
-//   Y(t): mask, row max, lazy rescale, exp, P(t) -> bf16      (VALU)
+// One workgroup = 8 waves = 256 query rows of one head; key tiles of
+// TK = 64 * NSUB keys (128 when the chunk size allows: half the phase
+// barriers per key, 2-3 % faster than 64).  Waves 0-3 (group 0) and 4-7
+// (group 1) share the four SIMDs one-to-one and alternate, phase by phase,
+// between
+//   X(t): O^T += V(t-1)^T P(t-1)^T, then S^T(t) = K(t) Q^T    (TK/2 MFMAs)
+//   Y(t): mask, exp, P(t) -> bf16, row sums, lazy rescale     (VALU)
 // with group 1 one phase behind group 0, so each SIMD has one wave feeding the
 // matrix core while the other runs the softmax (the hardware co-issues them;
 // measured 4% faster than four independent waves per workgroup, and raising
 // the MFMA wave's priority made it slower).  Phases end at a workgroup
 // barrier.  K(t+1) and V(t) are loaded straight into LDS at the
 // start of phase 2t and waited for at the end of phase 2t+1; K and V are each
-// double-buffered.  With s a multiple of 64 every 32-row wave block lies in
-// one chunk and every 64-key tile in one chunk, so a (wave, tile) pair has a
+// double-buffered.  With s a multiple of TK every 32-row wave block lies in
+// one chunk and every key tile in one chunk, so a (wave, tile) pair has a
 // single relation and no straddle handling is needed.
 // Maximum of a lane's 32 scores as a tree of max3 (depth 4), so the wave is
 // not held up by a 16-deep dependency chain.
@@ -376,6 +378,35 @@ __device__ inline float max32(const f32x16 (&x)[2]) {
 }
 
 constexpr int PP_BR = 256;
+
+// LDS of the two-group kernel for key tiles of TK = 64 * NSUB keys: K rows
+// (padded), then the V tile as NSUB sub-tiles of 64 keys, each [D][64]
+// transposed exactly as the V layout in HBM holds it (padded rows); two
+// buffers of each.
+template <int D, int NSUB>
+struct PPSmem {
+  static constexpr int TK = 64 * NSUB;
+  static constexpr int KROW = D * 2 + 16;
+  static constexpr int VROW = 64 * 2 + 16;
+  static constexpr int KBYTES = TK * KROW;
+  static constexpr int VSUB = D * VROW;
+  static constexpr int VBYTES = NSUB * VSUB;
+  static constexpr int KPIECES = KBYTES / 1024;
+  static constexpr int VPIECES = VSUB / 1024;   // per sub-tile
+  static constexpr int TOTAL = 2 * (KBYTES + VBYTES);
+  static_assert(KBYTES % 1024 == 0 && VSUB % 1024 == 0, "tiles must be whole 1 KiB pieces");
+};
+
+// Row max over the 32 * NSUB scores a lane holds.
+template <int NSUB>
+__device__ inline float max_tile(const f32x16 (&x)[2 * NSUB]) {
+  if constexpr (NSUB == 1) {
+    return max32(x);
+  } else {
+    const f32x16 lo[2] = {x[0], x[1]}, hi[2] = {x[2], x[3]};
+    return fmaxf(max32(lo), max32(hi));
+  }
+}
 constexpr float kSumLimit = 256.0f;  // per-lane probability sum that forces a rescale
 // Word 3 of a raw buffer descriptor on gfx9-family parts (gfx950): 32-bit
 // data format, no swizzle, offsets bounded by the record count in word 2.
@@ -387,14 +418,16 @@ constexpr int kBufferWord3 = 0x00020000;
 // data is only needed two phases later.
 __device__ inline void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D, int MAP>
+template <int D, int MAP, int NSUB>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<D>::TOTAL];
+  using SM = PPSmem<D, NSUB>;
+  constexpr int TK = SM::TK;   // keys per tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
   // LDS: K buffers 0/1 then V buffers 0/1.
-  constexpr int KB0 = 0, VB0 = 2 * Smem<D>::KBYTES;
+  constexpr int KB0 = 0, VB0 = 2 * SM::KBYTES;
 
   // ---- work item (longest causal rows first, XCD-aware GQA grouping) ----------
   const int wg = blockIdx.x;
@@ -437,7 +470,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const int qrow = i_lo + ql;
   const int nq = i_lo / s;                 // the wave's 32 rows share one chunk
   const int rq = qrow - nq * s;
-  const int nkt = min(i0 + PP_BR - 1, L - 1) / BC + 1;
+  const int nkt = min(i0 + PP_BR - 1, L - 1) / TK + 1;
 
   // ---- order in which key tiles are visited ("virtual tiles" t) -------------
   // DCA: key tiles 0 .. nkt-1; a (wave, tile) pair has one chunk relation.
@@ -457,13 +490,13 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   if constexpr (MAP == kMapSelfExtend) {
     const int W = a.se_window;
     const int i_top = min(i0 + PP_BR - 1, L - 1);
-    n_gr = i_top >= W ? (i_top - W) / BC + 1 : 0;
-    nb_begin = max(i0 - W + 1, 0) / BC;
+    n_gr = i_top >= W ? (i_top - W) / TK + 1 : 0;
+    nb_begin = max(i0 - W + 1, 0) / TK;
     nvt = n_gr + (W > 0 ? nkt - nb_begin : 0);
   } else if constexpr (MAP == kMapCoarseFine) {
     const int c_first = i0 / s, c_last = min(i0 + PP_BR - 1, L - 1) / s;
-    n_gr = c_last >= 2 ? (c_last - 1) * (s / BC) : 0;
-    nb_begin = max(c_first - 1, 0) * (s / BC);
+    n_gr = c_last >= 2 ? (c_last - 1) * (s / TK) : 0;
+    nb_begin = max(c_first - 1, 0) * (s / TK);
     nvt = n_gr + nkt - nb_begin;
   }
   auto tile_of = [&](int t) __attribute__((always_inline)) {
@@ -475,12 +508,12 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // for masked tiles so the variant only moves inter -> successive -> intra.
   auto class_of = [&](int t) __attribute__((always_inline)) {
     if constexpr (MAP == kMapSelfExtend) return t < n_gr ? kSeGrouped : kSeNeighbor;
-    if constexpr (MAP == kMapCoarseFine) return t < n_gr ? 2 : min(max(nq - (tile_of(t) * BC) / s, 0), 1);
-    return min(nq - (t * BC) / s, 2);
+    if constexpr (MAP == kMapCoarseFine) return t < n_gr ? 2 : min(max(nq - (tile_of(t) * TK) / s, 0), 1);
+    return min(nq - (t * TK) / s, 2);
   };
   // Coarse / fine: does this wave keep virtual tile t at all (else p = 0)?
   auto cf_keep = [&](int t) __attribute__((always_inline)) {
-    const int rho = nq - (tile_of(t) * BC) / s;
+    const int rho = nq - (tile_of(t) * TK) / s;
     return t < n_gr ? rho >= 2 : (rho == 0 || rho == 1);
   };
 
@@ -525,23 +558,24 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   };
 
   // ---- direct-to-LDS staging, 1-KiB pieces round-robin over the 8 waves -----
-  constexpr int KPW = (Smem<D>::KPIECES + 7) / 8;
-  constexpr int VPW = (Smem<D>::VPIECES + 7) / 8;
+  constexpr int KPW = (SM::KPIECES + 7) / 8;
+  constexpr int VPW = (SM::VPIECES + 7) / 8;
   uint32_t koff[KPW], voff[VPW];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int byte = (wave + 8 * i) * 1024 + lane * 16;
-    const int row = byte / Smem<D>::KROW, w = byte % Smem<D>::KROW;
+    const int row = byte / SM::KROW, w = byte % SM::KROW;
     koff[i] = (uint32_t)(row * D * 2 + (w < D * 2 ? w : 0));
   }
 #pragma unroll
   for (int i = 0; i < VPW; ++i) {
     const int byte = (wave + 8 * i) * 1024 + lane * 16;
-    const int row = byte / Smem<D>::VROW, w = byte % Smem<D>::VROW;
-    voff[i] = (uint32_t)(row * BC * 2 + (w < BC * 2 ? w : 0));
+    const int row = byte / SM::VROW, w = byte % SM::VROW;
+    voff[i] = (uint32_t)(row * 64 * 2 + (w < 64 * 2 ? w : 0));
   }
   // K/V tiles go straight to LDS through buffer loads (MUBUF with the lds
-  // bit).  The descriptor covers this head's Lp rows exactly.  The FLAT form
+  // bit).  The descriptor covers this head's Lp rows exactly (Lp is a
+  // multiple of the widest tile, so no tile reaches past it).  The FLAT form
   // of the same DMA would make the compiler wait for every outstanding LDS
   // read (lgkmcnt(0)) while it is in flight.
   const uint32_t head_bytes = (uint32_t)((int64_t)a.Lp * D * 2);
@@ -553,8 +587,8 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     krsrc2 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint16_t*)a.krot2 + bg * (int64_t)a.Lp * D), (short)0, head_bytes, kBufferWord3);
   auto issue_k = [&](int t) {
-    const int soff = tile_of(t) * BC * D * 2;
-    uint8_t* dst = smem + KB0 + (t & 1) * Smem<D>::KBYTES;
+    const int soff = tile_of(t) * TK * D * 2;
+    uint8_t* dst = smem + KB0 + (t & 1) * SM::KBYTES;
     __amdgpu_buffer_rsrc_t rs = krsrc;
     if constexpr (MAP == kMapSelfExtend)
       if (class_of(t) == kSeGrouped) rs = krsrc2;
@@ -562,66 +596,74 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
       if (t < n_gr) rs = krsrc2;   // the scaled-key pass (same for every wave)
 #pragma unroll
     for (int i = 0; i < KPW; ++i)
-      if (wave + 8 * i < Smem<D>::KPIECES)
+      if (wave + 8 * i < SM::KPIECES)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
                                                  16, (int)koff[i], soff, 0, 0);
   };
+  // V: NSUB consecutive 64-key tiles of the HBM layout.
   auto issue_v = [&](int t) {
-    const int soff = tile_of(t) * BC * D * 2;
-    uint8_t* dst = smem + VB0 + (t & 1) * Smem<D>::VBYTES;
 #pragma unroll
-    for (int i = 0; i < VPW; ++i)
-      if (wave + 8 * i < Smem<D>::VPIECES)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
-                                                 16, (int)voff[i], soff, 0, 0);
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int soff = (tile_of(t) * NSUB + sub) * 64 * D * 2;
+      uint8_t* dst = smem + VB0 + (t & 1) * SM::VBYTES + sub * SM::VSUB;
+#pragma unroll
+      for (int i = 0; i < VPW; ++i)
+        if (wave + 8 * i < SM::VPIECES)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
+                                                   16, (int)voff[i], soff, 0, 0);
+    }
   };
-  const int kfrag = ql * Smem<D>::KROW + hh * 16;
-  const int vfrag = ql * Smem<D>::VROW + hh * 16;
+  const int kfrag = ql * SM::KROW + hh * 16;
+  const int vfrag = ql * SM::VROW + hh * 16;
+  // LDS offset of the PV operand fragment for 16-key group g4 and 32-dim block db
+  auto voffs = [](int g4, int db) constexpr { return (g4 >> 2) * SM::VSUB + db * 32 * SM::VROW + (g4 & 3) * 32; };
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-  f32x16 sacc[2];
-  bf16x8 pf[4];
+  f32x16 sacc[2 * NSUB];
+  bf16x8 pf[4 * NSUB];
   float m_run = kNoMax, l_run = 0.f;
   int cur_cls = -1;
 
   auto do_pv = [&](int t) {
-    const uint8_t* vb = smem + VB0 + (t & 1) * Smem<D>::VBYTES + vfrag;
+    const uint8_t* vb = smem + VB0 + (t & 1) * SM::VBYTES + vfrag;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
+    for (int g4 = 0; g4 < 4 * NSUB; ++g4)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x8 vf = *(const bf16x8*)(vb + db * 32 * Smem<D>::VROW + g4 * 32);
+        const bf16x8 vf = *(const bf16x8*)(vb + voffs(g4, db));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g4], oacc[db], 0, 0, 0);
       }
   };
   auto do_qk = [&](int t) {
-    const uint8_t* kb = smem + KB0 + (t & 1) * Smem<D>::KBYTES + kfrag;
+    const uint8_t* kb = smem + KB0 + (t & 1) * SM::KBYTES + kfrag;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
+    for (int kb2 = 0; kb2 < 2 * NSUB; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[kb2][v] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 kf = *(const bf16x8*)(kb + kb2 * 32 * Smem<D>::KROW + ds * 32);
+      for (int kb2 = 0; kb2 < 2 * NSUB; ++kb2) {
+        const bf16x8 kf = *(const bf16x8*)(kb + kb2 * 32 * SM::KROW + ds * 32);
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb2], 0, 0, 0);
       }
   };
   auto do_softmax = [&](int t) {
-    const int j0 = tile_of(t) * BC;
+    const int j0 = tile_of(t) * TK;
     // Keys this lane keeps: [lo, hi].  DCA: the causal prefix.  SelfExtend:
     // grouped j <= i - W, neighbor i - W < j <= i.  The mask is applied only
     // when the tile is not wholly inside every row's range.
     int lo = 0, hi = qrow;
-    bool need = j0 + BC - 1 > i_lo;
+    bool need = j0 + TK - 1 > i_lo;
     if constexpr (MAP == kMapSelfExtend) {
       const int W = a.se_window;
       if (class_of(t) == kSeGrouped) {
         hi = qrow - W;
-        need = j0 + BC - 1 > i_lo - W;
+        need = j0 + TK - 1 > i_lo - W;
       } else {
         lo = qrow - W + 1;
         need = need || j0 < i_lo + 32 - W;
@@ -637,38 +679,38 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     if (need) {
       const int jb = j0 + hh * 4;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2 * NSUB; ++kb2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = jb + kb2 * 32 + (v >> 2) * 8 + (v & 3);
           sacc[kb2][v] = (j >= lo && j <= hi) ? sacc[kb2][v] : -INFINITY;
         }
     }
-    // Probabilities against the running max first.  A lane whose 32
+    // Probabilities against the running max first.  A lane whose 32 * NSUB
     // probabilities sum past 2^8 (or to inf on the first tile, where the
     // running max is the sentinel) sends the wave through the exact rescale:
     // the true max, the accumulator rescale and the exps again.  Every stored
     // probability is therefore at most 2^8 and O and l share one max.
     auto exps = [&]() {
-      float lsum[4];
+      float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
+      for (int g4 = 0; g4 < 4 * NSUB; ++g4) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g4 >> 1][(g4 & 1) * 8 + e], scale_log2, -m_run));
         const uint4 pu = pack_bf16x8(p);
-        float ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, 0.f, false);
+        float ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum[g4 & 3], false);
         ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, ls, false);
         ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, ls, false);
-        lsum[g4] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, ls, false);
+        lsum[g4 & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, ls, false);
         pf[g4] = as_bf16x8(pu);
       }
       return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
     float lt = exps();
     if (__any(!(lt <= kSumLimit))) {
-      const float mnew = max_halves(max32(sacc)) * scale_log2;
+      const float mnew = max_halves(max_tile<NSUB>(sacc)) * scale_log2;
       const float mn = fmaxf(m_run, mnew);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
       l_run *= alpha;
@@ -686,6 +728,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // compiler sinks their exps past the phase barrier, next to that use.
   auto pin_p = [&]() {
     asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
+    if constexpr (NSUB == 2) asm volatile("" : "+v"(pf[4]), "+v"(pf[5]), "+v"(pf[6]), "+v"(pf[7]));
   };
 
   // ---- phases ---------------------------------------------------------------
@@ -704,22 +747,25 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // MFMA waits only for the oldest read in flight.
   auto x_full = [&](int t) {
     prep_q(t);
-    constexpr int NPV = 4 * NDB, NQK = 2 * NDS, NX = NPV + NQK, NPRE = 6;
-    const uint8_t* vb = smem + VB0 + ((t - 1) & 1) * Smem<D>::VBYTES + vfrag;
-    const uint8_t* kb = smem + KB0 + (t & 1) * Smem<D>::KBYTES + kfrag;
+    constexpr int NKB = 2 * NSUB;   // 32-key blocks per tile
+    constexpr int NPV = 4 * NSUB * NDB, NQK = NKB * NDS, NX = NPV + NQK, NPRE = 6;
+    const uint8_t* vb = smem + VB0 + ((t - 1) & 1) * SM::VBYTES + vfrag;
+    const uint8_t* kb = smem + KB0 + (t & 1) * SM::KBYTES + kfrag;
     auto frag = [&](int i) -> bf16x8 {
       if (i < NPV) {
         const int g4 = i / NDB, db = i % NDB;
-        return *(const bf16x8*)(vb + db * 32 * Smem<D>::VROW + g4 * 32);
+        return *(const bf16x8*)(vb + voffs(g4, db));
       }
-      const int ds = (i - NPV) / 2, kb2 = (i - NPV) % 2;
-      return *(const bf16x8*)(kb + kb2 * 32 * Smem<D>::KROW + ds * 32);
+      const int ds = (i - NPV) / NKB, kb2 = (i - NPV) % NKB;
+      return *(const bf16x8*)(kb + kb2 * 32 * SM::KROW + ds * 32);
     };
     bf16x8 ring[NPRE];
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) ring[i] = frag(i);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[kb2][v] = 0.f;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const bf16x8 f = ring[i % NPRE];
@@ -728,7 +774,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         const int g4 = i / NDB, db = i % NDB;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[g4], oacc[db], 0, 0, 0);
       } else {
-        const int ds = (i - NPV) / 2, kb2 = (i - NPV) % 2;
+        const int ds = (i - NPV) / NKB, kb2 = (i - NPV) % NKB;
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[ds], sacc[kb2], 0, 0, 0);
       }
     }
@@ -947,34 +993,39 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillArgs a) {
 
 }  // namespace
 
+// The two-group kernel at one map and tile width, either head dim.
+template <int MAP, int NSUB>
+void launch_pp(const PrefillArgs& a, dim3 grid, int nqt, int xcd_map, float scale_log2, hipStream_t st) {
+  if (a.D == 64)
+    hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, MAP, NSUB>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+  else
+    hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, MAP, NSUB>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   const int xcd_map = ((int64_t)a.B * a.Hkv) % 8 == 0 ? 1 : 0;
   const float scale_log2 = a.sm_scale * kLog2e;
-  // DCA takes the ping-pong kernel when every 32-row wave block and 64-key
+  // DCA takes the two-group kernel when every 32-row wave block and 64-key
   // tile lies inside one chunk: s a multiple of 64 and query offsets
-  // multiples of 32.  SelfExtend always does.
-  bool pp = a.s % BC == 0;
+  // multiples of 32.  SelfExtend always does.  128-key tiles (half the phase
+  // barriers per key) whenever the chunk size allows them.
+  bool pp = a.s % 64 == 0;
   if (a.per_seq)
     for (int i = 0; i < a.B; ++i) pp = pp && a.seq_q0[i] % 32 == 0;
   if (a.map == kMapCoarseFine && !pp) return hipErrorInvalidValue;   // needs chunk % 64 == 0 (host-checked)
   if (a.map != kMapDCA || pp) {
+    const bool wide = a.Lp % 128 == 0 && (a.map == kMapSelfExtend || a.s % 128 == 0);
     const int nqt = (a.q_rows + PP_BR - 1) / PP_BR;
     const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
     if (a.map == kMapSelfExtend) {
-      if (a.D == 64)
-        hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapSelfExtend>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
-      else
-        hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapSelfExtend>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+      if (wide) launch_pp<kMapSelfExtend, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+      else launch_pp<kMapSelfExtend, 1>(a, grid, nqt, xcd_map, scale_log2, st);
     } else if (a.map == kMapCoarseFine) {
-      if (a.D == 64)
-        hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapCoarseFine>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
-      else
-        hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapCoarseFine>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+      if (wide) launch_pp<kMapCoarseFine, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+      else launch_pp<kMapCoarseFine, 1>(a, grid, nqt, xcd_map, scale_log2, st);
     } else {
-      if (a.D == 64)
-        hipLaunchKernelGGL((prefill_bf16_pp_kernel<64, kMapDCA>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
-      else
-        hipLaunchKernelGGL((prefill_bf16_pp_kernel<128, kMapDCA>), grid, dim3(512), 0, st, a, nqt, xcd_map, scale_log2);
+      if (wide) launch_pp<kMapDCA, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+      else launch_pp<kMapDCA, 1>(a, grid, nqt, xcd_map, scale_log2, st);
     }
     return hipGetLastError();
   }

@@ -107,13 +107,23 @@ def test_selfextend_group_swap_invariance():
 
 
 def test_selfextend_deterministic_and_causal():
+    # Rows before a cut do not depend on the keys / values after it.  A wave
+    # owns 32 rows and takes its exact-rescale decision for all of them, so a
+    # row sharing a wave with changed rows may be computed through the exact
+    # path instead (the same value up to rounding); rows of other waves are
+    # bit-identical.
     q, k, v = (x.to(dev()) for x in inputs.prefill_inputs(1, 777, 4, 1, 128, "bf16", seed=9, qk_scale=2.0))
     o1 = dca.selfextend_prefill(q, k, v, 8, 128)
     assert torch.equal(o1, dca.selfextend_prefill(q, k, v, 8, 128))
-    k2, v2 = k.clone(), v.clone()
-    k2[:, 500:] = 3.0
-    v2[:, 500:] = -2.0
-    assert torch.equal(o1[:, :500], dca.selfextend_prefill(q, k2, v2, 8, 128)[:, :500])
+    for cut in (512, 500):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, cut:] = 3.0
+        v2[:, cut:] = -2.0
+        o2 = dca.selfextend_prefill(q, k2, v2, 8, 128)
+        whole = cut // 32 * 32   # rows in waves wholly before the cut
+        assert torch.equal(o1[:, :whole], o2[:, :whole]), cut
+        if whole < cut:
+            assert (o1[:, whole:cut].float() - o2[:, whole:cut].float()).abs().max() <= 2e-2, cut
 
 
 def test_selfextend_32k_workload_sampled_rows():
