@@ -75,7 +75,10 @@ def measured_traffic(key):
 
 def prefill_kernel_name(c, w, D):
     """The attention kernel the library launches for bf16 (chunk size s = c - w)."""
-    return f"prefill_bf16_pp_kernel<{D}, 0>" if (c - w) % 64 == 0 else f"prefill_bf16_kernel<{D}>"
+    s = c - w
+    if s % 128 == 0:
+        return f"prefill_bf16_pp_kernel<{D}, 0, 2>"
+    return f"prefill_bf16_pp_kernel<{D}, 0, 1>" if s % 64 == 0 else f"prefill_bf16_kernel<{D}>"
 
 
 def cpu_baseline(q, k, v, cfg, seconds):
