@@ -236,13 +236,17 @@ def main():
                               "traffic": measured_traffic("prefill_attend"),
                               "kernel": prefill_kernel_name(P["c"], P["w"], P["D"]),
                               "kernel_ms": att_ms, "flops_per_launch": fl}
+        att_all = sorted(e[1].elapsed_time(e[2]) for e in pe)
         result["prefill_32k"] = {"ms": prep_ms + att_ms, "prepare_ms": prep_ms, "attend_ms": att_ms,
+                                 "attend_ms_median": att_all[len(att_all) // 2], "attend_ms_min": att_all[0],
                                  "tflops": result["value"]}
     if run_decode:
         dec_ms = sum(e[0].elapsed_time(e[1]) for e in de) / args.steps
         nb = decode_bytes(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"])
         gbps = nb / (dec_ms * 1e-3) / 1e9
-        result["decode"] = {"ms": dec_ms, "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        dec_all = sorted(e[0].elapsed_time(e[1]) for e in de)
+        result["decode"] = {"ms": dec_ms, "ms_median": dec_all[len(dec_all) // 2], "ms_min": dec_all[0],
+                            "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": gbps / PEAK_HBM_GBPS, "bytes_per_call": nb, "bound": "hbm",
                             "traffic": measured_traffic("decode_split")}
         if not run_prefill:

@@ -2,7 +2,8 @@
 benchmark times, on rows the oracle evaluates one by one.
 
 Rows: the chunk-geometry landmarks {0, 1, s-1, s, s+w-1, s+w, 2s-1, 2s,
-2s+w-1, 2s+w, c-1, c, L-1} plus seeded random rows.  Bars: bf16 max-abs
+2s+w-1, 2s+w, c-1, c, L-1} plus 256 seeded random rows (128 at 131072
+tokens, on one query head per KV group).  Bars: bf16 max-abs
 <= 2e-2 and mean-abs <= 2e-3.
 """
 import sys
@@ -33,6 +34,19 @@ def landmark_rows(L, c, w, n_random, seed):
     return np.array(sorted(r for r in rows if 0 <= r < L))
 
 
+def lse_bound_rows(q, k, rows, heads):
+    """bf16 LSE bar on the sampled rows: max(2e-2, 2^-8 * scale * |q_i| *
+    max_{j<=i} |k_j|).  Rounding the rotated q and k to bf16 moves every score
+    by at most 2^-8 * scale * |q| |k| (rotations keep norms), and the LSE by at
+    most the largest score change."""
+    qn = torch.linalg.vector_norm(q[:, rows][:, :, heads], dim=-1, dtype=torch.float32).double().numpy()
+    kn = torch.linalg.vector_norm(k, dim=-1, dtype=torch.float32).double().numpy()       # [B, L, Hkv]
+    G = q.shape[2] // k.shape[2]
+    kmax = np.maximum.accumulate(kn, axis=1)[:, rows][:, :, np.asarray(heads) // G]      # [B, R, H]
+    bound = 2.0 ** -8 / np.sqrt(q.shape[-1]) * qn * kmax
+    return np.maximum(2e-2, bound.transpose(0, 2, 1))                                    # [B, H, R]
+
+
 def check(got, want, what):
     err = np.abs(got - want)
     mx, mean = float(err.max()), float(err.mean())
@@ -40,7 +54,7 @@ def check(got, want, what):
     assert mx <= BF16_MAX and mean <= BF16_MEAN, what
 
 
-def run_prefill_workload(name, heads=None, n_random=32, qk_scale=None, seed_offset=0):
+def run_prefill_workload(name, heads=None, n_random=256, qk_scale=None, seed_offset=0):
     cfg = inputs.WORKLOADS[name]
     B, L, Hq, Hkv, D, c, w = (cfg[k] for k in ("B", "L", "Hq", "Hkv", "D", "c", "w"))
     log(f"[{name}] generating inputs (seed {cfg['seed'] + seed_offset})")
@@ -58,7 +72,8 @@ def run_prefill_workload(name, heads=None, n_random=32, qk_scale=None, seed_offs
     log(f"[{name}] oracle on {len(rows)} rows x {len(heads)} heads")
     O, LSE = oracle.dca_prefill_ref(q, k, v, c, w, cfg["base"], rows=rows, heads=heads)
     check(og, O, f"{name} O")
-    assert np.abs(lg - LSE).max() <= 2e-2
+    lerr = np.abs(lg - LSE)
+    assert np.all(lerr <= lse_bound_rows(q, k, torch.from_numpy(rows), torch.from_numpy(heads))), lerr.max()
 
 
 def test_llama2_7b_16k_sampled_rows():
@@ -75,7 +90,7 @@ def test_llama2_70b_32k_sampled_rows():
 
 def test_llama2_70b_128k_sampled_rows():
     # one query head per KV group, landmark + random rows
-    run_prefill_workload("llama2_70b_128k", heads=[g * 8 + (g % 8) for g in range(8)], n_random=16)
+    run_prefill_workload("llama2_70b_128k", heads=[g * 8 + (g % 8) for g in range(8)], n_random=128)
 
 
 def test_decode_100k_sampled_batches():
