@@ -40,6 +40,7 @@ from .selfextend_ref import (  # noqa: F401
     se_rope_remap_ref,
     selfextend_prefill_ref,
     selfextend_prefill_formB,
+    selfextend_decode_ref,
 )
 from .coarse_fine_ref import (  # noqa: F401
     coarse_fine_distance_table,
@@ -47,4 +48,6 @@ from .coarse_fine_ref import (  # noqa: F401
     coarse_fine_key_positions,
     coarse_fine_prefill_ref,
     coarse_fine_prefill_formB,
+    coarse_fine_key_remap_ref,
+    coarse_fine_decode_ref,
 )

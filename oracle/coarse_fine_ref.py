@@ -144,3 +144,52 @@ def coarse_fine_prefill_formB(q, k, v, C: int, train_len: int, target_len: int, 
                 O[b, i, h] = o[0]
                 LSE[b, h, i] = lse[0]
     return O, LSE
+
+
+def coarse_fine_key_remap_ref(x, pos0: int, C: int, train_len: int, target_len: int,
+                              base: float = 10000.0) -> np.ndarray:
+    """Keys rotated at their coarse-scaled positions floor(p/C) C / kappa + p mod C
+    (the rotation every key takes in pairs two or more chunks apart), for the
+    rows of x [B, L, H, D] at positions pos0 .. pos0 + L - 1."""
+    x = _f64(x)
+    L = x.shape[1]
+    _, p = coarse_fine_key_positions(pos0 + np.arange(L), C, train_len, target_len)
+    return rope_rotate(x, p[None, :, None], base)
+
+
+def coarse_fine_decode_ref(q, k_raw, v, kv_len, C: int, train_len: int, target_len: int,
+                           base: float = 10000.0, sm_scale: float | None = None):
+    """Decode under the coarse / fine map: sequence b's new token is row
+    kv_len[b] - 1 of the prefill definition over its first kv_len[b] keys.
+    q: [B, Hq, D] raw; k_raw, v: [B, cache_len, Hkv, D] raw.
+    Returns O [B, Hq, D] and LSE [B, Hq]."""
+    q = _f64(q)
+    B, Hq, D = q.shape
+    Hkv = k_raw.shape[2]
+    scale = 1.0 / np.sqrt(D) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    O = np.zeros((B, Hq, D))
+    LSE = np.zeros((B, Hq))
+    for b in range(B):
+        n = int(kv_len[b])
+        i = n - 1
+        c = i // C
+        kp_plain, kp_scaled = coarse_fine_key_positions(np.arange(n), C, train_len, target_len)
+        p_intra, p_succ, p_inter = coarse_fine_positions(i, C, train_len, target_len)
+        for g in range(Hkv):
+            kb = _f64(k_raw[b, :n, g])
+            k_pl, k_sc = rope_rotate(kb, kp_plain, base), rope_rotate(kb, kp_scaled, base)
+            vb = _f64(v[b, :n, g])
+            for h in range(Hq):
+                if _kv_head(h, Hq, Hkv) != g:
+                    continue
+                S = np.empty(n)
+                for lo, hi_, pq, khat in ((c * C, n, p_intra, k_pl), ((c - 1) * C, c * C, p_succ, k_pl),
+                                          (0, (c - 1) * C, p_inter, k_sc)):
+                    lo = max(lo, 0)
+                    if hi_ <= lo:
+                        continue
+                    S[lo:hi_] = scale * (khat[lo:hi_] @ rope_rotate(q[b, h], pq, base))
+                o, lse = _softmax_rows(S[None, :], vb)
+                O[b, h] = o[0]
+                LSE[b, h] = lse[0]
+    return O, LSE

@@ -167,3 +167,41 @@ def selfextend_prefill_formB(q, k, v, G: int, W: int, base: float = 10000.0,
                 O[b, i, h] = o[0]
                 LSE[b, h, i] = lse[0]
     return O, LSE
+
+
+def selfextend_decode_ref(q, k_raw, v, kv_len, G: int, W: int, base: float = 10000.0,
+                          sm_scale: float | None = None):
+    """Decode under the SelfExtend map: sequence b's new token is row
+    kv_len[b] - 1 of the prefill definition over its first kv_len[b] cached
+    keys.  q: [B, Hq, D] raw; k_raw, v: [B, cache_len, Hkv, D] raw.
+    Returns O [B, Hq, D] and LSE [B, Hq]."""
+    _check(G, W)
+    q = _f64(q)
+    B, Hq, D = q.shape
+    Hkv = k_raw.shape[2]
+    scale = 1.0 / np.sqrt(D) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    O = np.zeros((B, Hq, D))
+    LSE = np.zeros((B, Hq))
+    for b in range(B):
+        n = int(kv_len[b])
+        i = n - 1
+        jj = np.arange(n)
+        rel = se_relation(i, jj, W)
+        for g in range(Hkv):
+            kb = _f64(k_raw[b, :n, g])
+            k_nb = rope_rotate(kb, se_key_position(jj, G, NEIGHBOR), base)
+            k_gr = rope_rotate(kb, se_key_position(jj, G, GROUPED), base)
+            vb = _f64(v[b, :n, g])
+            for h in range(Hq):
+                if _kv_head(h, Hq, Hkv) != g:
+                    continue
+                S = np.empty(n)
+                for r_kind, khat in ((NEIGHBOR, k_nb), (GROUPED, k_gr)):
+                    sel = rel == r_kind
+                    if sel.any():
+                        qv = rope_rotate(q[b, h], se_query_position(i, G, W, r_kind), base)
+                        S[sel] = scale * (khat[sel] @ qv)
+                o, lse = _softmax_rows(S[None, :], vb)
+                O[b, h] = o[0]
+                LSE[b, h] = lse[0]
+    return O, LSE

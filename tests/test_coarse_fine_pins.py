@@ -159,3 +159,38 @@ def test_pins_catch_a_scaled_fine_offset(monkeypatch):
     monkeypatch.setattr(cf, "coarse_fine_positions", wrong)
     with pytest.raises(AssertionError):
         test_guide_far_pair_and_bound_by_hand()
+
+
+@pytest.mark.parametrize("C,train,target", [(16, 4, 8), (12, 3, 7), (8, 2, 2)])
+def test_decode_is_the_last_prefill_row(C, train, target):
+    kv = [1, 20, 61, 50]
+    B, L, Hq, Hkv, D = len(kv), max(kv), 4, 2, 16
+    q, k, v = (x.double().numpy() for x in inputs.prefill_inputs(B, L, Hq, Hkv, D, "f32", seed=62, qk_scale=2.0))
+    qd = np.stack([q[b, kv[b] - 1] for b in range(B)])
+    O, LSE = cf.coarse_fine_decode_ref(qd, k, v, kv, C, train, target)
+    for b in range(B):
+        n = kv[b]
+        Op, Lp = cf.coarse_fine_prefill_ref(q[b: b + 1, :n], k[b: b + 1, :n], v[b: b + 1, :n], C, train, target,
+                                            rows=[n - 1])
+        assert np.abs(O[b] - Op[0, 0]).max() < 1e-12 and np.abs(LSE[b] - Lp[0, :, 0]).max() < 1e-12
+
+
+def test_scaled_key_remap_gives_the_guide_distances():
+    # For a pair two or more chunks apart, the inter query position against the
+    # remapped key reproduces the guide's distance: <R_{P_inter(i)} q, remap(k)_j>
+    # = q . R_{-M(i, j)} k with M from the per-pair formulas.
+    C, train, target, L, D = 10, 3, 8, 47, 8
+    rng = np.random.default_rng(63)
+    q = rng.standard_normal(D)
+    k = rng.standard_normal((1, L, 1, D))
+    kr = cf.coarse_fine_key_remap_ref(k, 0, C, train, target)[0, :, 0]
+    M = cf.coarse_fine_distance_table(L, C, train, target)
+    i = L - 1
+    _, _, p_inter = cf.coarse_fine_positions(i, C, train, target)
+    qr = _rope_complex(q, p_inter, 1e4)
+    for j in range(0, (i // C - 1) * C):
+        want = float(q @ _rope_complex(k[0, j, 0], -M[i, j], 1e4))
+        assert abs(float(qr @ kr[j]) - want) < 1e-9, j
+    # pos0 shifts the positions: rows of a later slice match the whole remap
+    whole = cf.coarse_fine_key_remap_ref(k, 0, C, train, target)
+    assert np.abs(cf.coarse_fine_key_remap_ref(k[:, 13:], 13, C, train, target) - whole[:, 13:]).max() < 1e-12

@@ -180,3 +180,18 @@ def test_pins_catch_an_off_by_one_window(monkeypatch):
 def test_pins_catch_ungrouped_keys(monkeypatch):
     monkeypatch.setattr(se, "se_key_position", lambda j, G, rel: np.asarray(j, dtype=np.int64))
     assert _caught()
+
+
+@pytest.mark.parametrize("G,W", [(4, 16), (3, 0), (1, 7), (5, 200)])
+def test_decode_is_the_last_prefill_row(G, W):
+    # A ragged batch: sequence b decodes its token kv[b] - 1 over its first kv[b] keys.
+    kv = [1, 37, 90, 64]
+    B, L, Hq, Hkv, D = len(kv), max(kv), 4, 2, 16
+    q, k, v = (x.double().numpy() for x in inputs.prefill_inputs(B, L, Hq, Hkv, D, "f32", seed=61, qk_scale=2.0))
+    qd = np.stack([q[b, kv[b] - 1] for b in range(B)])
+    O, LSE = oracle.selfextend_decode_ref(qd, k, v, kv, G, W)
+    for b in range(B):
+        n = kv[b]
+        Op, Lp = oracle.selfextend_prefill_ref(q[b: b + 1, :n], k[b: b + 1, :n], v[b: b + 1, :n], G, W,
+                                               rows=[n - 1])
+        assert np.abs(O[b] - Op[0, 0]).max() < 1e-12 and np.abs(LSE[b] - Lp[0, :, 0]).max() < 1e-12
