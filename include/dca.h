@@ -354,6 +354,49 @@ int dca_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pa
                             int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
                             size_t ws_bytes, void* stream);
 
+/*
+ * Decode under the SelfExtend and coarse / fine maps.
+ *
+ * Definition: the new token of sequence b is row kv_len[b] - 1 of
+ * dca_selfextend_prefill (resp. dca_coarse_fine_prefill) over its first
+ * kv_len[b] cached tokens ("LLM Maybe LongLM: Self-Extend LLM Context Window
+ * Without Tuning", abstract; "Dual-Chunk Attention: Training-Free 100k+
+ * Context Guide", sections "Inter-Chunk Attention" and "Successive Chunk
+ * Smoothing"), computed split-K like dca_decode_varlen.  Both maps give a key
+ * one of two rotations, so the caller keeps two rotated key caches:
+ *   SelfExtend:    k_cache at j (dca_rope_remap DCA_MAP_PLAIN) for the
+ *                  neighbor keys j > q_pos - W, k_cache_grouped at floor(j/G)
+ *                  (DCA_MAP_SE_KEY_GROUPED, c = G, w = W) for the others;
+ *   coarse / fine: k_cache at j (DCA_MAP_PLAIN) for keys in the new token's
+ *                  chunk and the one before, k_cache_scaled at
+ *                  floor(j/C) C/kappa + j mod C (dca_coarse_fine_key_remap)
+ *                  for older keys.
+ * Each key is read from one of the two caches only.  q [B, Hq, D] raw;
+ * caches and v_cache [B, cache_len, Hkv, D]; kv_len HOST array (1 <=
+ * kv_len[b] <= cache_len); o, lse, sm_scale, GQA, dtypes and errors as in
+ * dca_decode_varlen.  The workspace queries return 0 on invalid sizes.
+ *
+ * dca_coarse_fine_key_remap: x [B, L, H, D] at positions pos0 .. pos0 + L - 1
+ * rotated at the coarse-scaled key positions (fp64 angles, one rounding),
+ * written to out (may alias x only if identical).
+ */
+size_t dca_selfextend_decode_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
+                                             int64_t D, int group, int window, int dtype);
+int dca_selfextend_decode(const void* q, const void* k_cache, const void* k_cache_grouped, const void* v_cache,
+                          void* o, float* lse, const int64_t* kv_len, int64_t B, int64_t cache_len,
+                          int64_t Hq, int64_t Hkv, int64_t D, int group, int window, double rope_base,
+                          float sm_scale, int dtype, void* ws, size_t ws_bytes, void* stream);
+size_t dca_coarse_fine_decode_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
+                                              int64_t D, int chunk, int dtype);
+int dca_coarse_fine_decode(const void* q, const void* k_cache, const void* k_cache_scaled, const void* v_cache,
+                           void* o, float* lse, const int64_t* kv_len, int64_t B, int64_t cache_len,
+                           int64_t Hq, int64_t Hkv, int64_t D, int chunk, int train_len, int target_len,
+                           double rope_base, float sm_scale, int dtype, void* ws, size_t ws_bytes,
+                           void* stream);
+int dca_coarse_fine_key_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
+                              int64_t pos0, int chunk, int train_len, int target_len, double rope_base,
+                              int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -389,6 +389,64 @@ def prefill_chunk_paged(q, k_pages, v_pages, block_table, pos0, c: int, w: int, 
     return (o, lse) if return_lse else o
 
 
+def _map_decode(fn_ws, fn, q, k_cache, k2, v_cache, kv_len, params, base, sm_scale, return_lse, workspace, name):
+    lib = _lib.load()
+    _check(q, "q", 3)
+    for t, n in ((k_cache, "k_cache"), (k2, name), (v_cache, "v_cache")):
+        _check(t, n, 4, q.dtype)
+    B, Hq, D = q.shape
+    cache_len, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, cache_len, Hkv, D) or v_cache.shape != k_cache.shape or k2.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    code = _dtype_code(q)
+    kl, _ = _host_i64(kv_len, B, "kv_len")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(getattr(lib, fn_ws)(kl, B, Hq, Hkv, D, *params[0], code))
+    if nbytes == 0:
+        raise ValueError("invalid decode sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check(fn, getattr(lib, fn)(
+        q.data_ptr(), k_cache.data_ptr(), k2.data_ptr(), v_cache.data_ptr(), o.data_ptr(), _ptr(lse), kl, B,
+        cache_len, Hq, Hkv, D, *params[1], float(base), float(sm_scale or 0.0), code, ws.data_ptr(), nbytes,
+        _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def selfextend_decode(q, k_cache, k_cache_grouped, v_cache, kv_len, group: int, window: int,
+                      base: float = 10000.0, sm_scale: float | None = None, return_lse: bool = False,
+                      workspace=None):
+    """SelfExtend decode of a ragged batch: q [B, Hq, D] raw; k_cache rotated at j,
+    k_cache_grouped at floor(j / group), v_cache: [B, cache_len, Hkv, D]."""
+    return _map_decode("dca_selfextend_decode_workspace_bytes", "dca_selfextend_decode", q, k_cache,
+                       k_cache_grouped, v_cache, kv_len, ((group, window), (group, window)), base, sm_scale,
+                       return_lse, workspace, "k_cache_grouped")
+
+
+def coarse_fine_decode(q, k_cache, k_cache_scaled, v_cache, kv_len, chunk: int, train_len: int, target_len: int,
+                       base: float = 10000.0, sm_scale: float | None = None, return_lse: bool = False,
+                       workspace=None):
+    """Coarse / fine map decode of a ragged batch: k_cache rotated at j, k_cache_scaled
+    at floor(j / chunk) * chunk * train_len / target_len + j mod chunk."""
+    return _map_decode("dca_coarse_fine_decode_workspace_bytes", "dca_coarse_fine_decode", q, k_cache,
+                       k_cache_scaled, v_cache, kv_len, ((chunk,), (chunk, train_len, target_len)), base,
+                       sm_scale, return_lse, workspace, "k_cache_scaled")
+
+
+def coarse_fine_key_remap(x, chunk: int, train_len: int, target_len: int, base: float = 10000.0, pos0: int = 0,
+                          out=None):
+    """Rotate x [B, L, H, D] (positions pos0 ..) at the coarse-scaled key positions."""
+    lib = _lib.load()
+    _check(x, "x", 4)
+    B, L, H, D = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _check(out, "out", 4, x.dtype)
+    _lib.check("dca_coarse_fine_key_remap", lib.dca_coarse_fine_key_remap(
+        x.data_ptr(), out.data_ptr(), B, L, H, D, int(pos0), chunk, train_len, target_len, float(base),
+        _dtype_code(x), _stream(x.device)))
+    return out
+
+
 def coarse_fine_prefill(q, k, v, chunk: int, train_len: int, target_len: int, base: float = 10000.0,
                         sm_scale: float | None = None, return_lse: bool = False, workspace=None):
     """Causal prefill under the DCA guide's coarse / fine distance map (chunk size,

@@ -58,6 +58,14 @@ SIGNATURES = {
                                 _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_prefill_chunk_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64,
                                        _i64, _i64, _i64, _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_selfextend_decode_workspace_bytes": (_sz, [_i64p, _i64, _i64, _i64, _i64, _int, _int, _int]),
+    "dca_selfextend_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _int,
+                                     _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_coarse_fine_decode_workspace_bytes": (_sz, [_i64p, _i64, _i64, _i64, _i64, _int, _int]),
+    "dca_coarse_fine_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _int,
+                                      _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_coarse_fine_key_remap": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _dbl, _int,
+                                         _vp]),
 }
 
 _lib = None

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "dca.h"
 #include "dca_launch.hpp"
 
@@ -80,14 +82,15 @@ struct DecodeLayout {
 };
 
 // kv: per-sequence cached key counts (host), or null for B sequences of
-// kv_len keys; kv_len is the longest sequence either way.
-bool decode_layout(int64_t B, const int64_t* kv, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
-                   int dtype, DecodeLayout* out) {
+// kv_len keys; kv_len is the longest sequence either way.  seg: per-sequence
+// key-segment boundaries (two key caches), or null.
+bool decode_layout(int64_t B, const int64_t* kv, const int64_t* seg, int64_t kv_len, int64_t Hq, int64_t Hkv,
+                   int64_t D, int dtype, DecodeLayout* out) {
   if (B < 1 || kv_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D) || !dtype_ok(dtype))
     return false;
   if (B >= kMaxDim || kv_len >= kMaxDim / 2 || Hq >= 65536 || B * Hq >= kMaxDim) return false;
   DecodeLayout p;
-  decode_plan(kv, B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
+  decode_plan(kv, seg, B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
   p.qv = 0;
   p.part_o = (size_t)round_up(B * Hq * 3 * D * elem_size(dtype), 256);
   p.part_lse = p.part_o + (size_t)round_up(B * Hq * (int64_t)p.ns * D * 4, 256);
@@ -438,7 +441,7 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
 size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
                                   int dtype) {
   DecodeLayout p;
-  return decode_layout(B, nullptr, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+  return decode_layout(B, nullptr, nullptr, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
 }
 
 int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -453,7 +456,7 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
       (lse && !aligned(lse, 4)))
     return DCA_ERR_INVALID_ARG;
   DecodeLayout p;
-  if (!decode_layout(B, nullptr, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!decode_layout(B, nullptr, nullptr, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
@@ -579,25 +582,65 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
 
 // Decode with per-sequence cache lengths over a dense cache (pg.bt null) or a
 // paged one (cache_len = the most rows a sequence's table covers).
+// The position map of a decode call.  SelfExtend and coarse / fine read the
+// keys below a per-sequence boundary from a second cache (kc2).
+struct DecodeMap {
+  int map = kMapDCA;
+  const void* kc2 = nullptr;
+  int se_group = 1, se_window = 0;
+  int cf_chunk = 1;
+  double cf_inv_kappa = 1.0;
+};
+
+// First key read from the main cache: SelfExtend, the first neighbor key of
+// the new token kv - 1 (j > kv - 1 - W); coarse / fine, the first key of the
+// chunk before the new token's chunk; DCA: 0.
+int64_t map_seg(const DecodeMap& m, int64_t kv) {
+  if (m.map == kMapSelfExtend) return kv - m.se_window > 0 ? kv - m.se_window : 0;
+  if (m.map == kMapCoarseFine) {
+    const int64_t ci = (kv - 1) / m.cf_chunk;
+    return ci >= 1 ? (ci - 1) * m.cf_chunk : 0;
+  }
+  return 0;
+}
+
+// Workspace layout of a ragged decode under a map (segments for two caches).
+bool map_decode_layout(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int dtype,
+                       const DecodeMap& m, DecodeLayout* p, std::vector<int64_t>* seg_out) {
+  if (!kv_len || B < 1 || B >= kMaxDim) return false;
+  int64_t max_kv = 0;
+  std::vector<int64_t> seg(m.map == kMapDCA ? 0 : (size_t)B);
+  for (int64_t b = 0; b < B; ++b) {
+    if (kv_len[b] < 1 || kv_len[b] >= kMaxDim / 2) return false;
+    max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
+    if (m.map != kMapDCA) seg[b] = map_seg(m, kv_len[b]);
+  }
+  if (!decode_layout(B, kv_len, seg.empty() ? nullptr : seg.data(), max_kv, Hq, Hkv, D, dtype, p)) return false;
+  if (seg_out) *seg_out = seg;
+  return true;
+}
+
 int decode_varlen_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                        const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
                        int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
-                       size_t ws_bytes, void* stream, const PagedKv& pg) {
+                       size_t ws_bytes, void* stream, const PagedKv& pg, const DecodeMap& dm = DecodeMap{}) {
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !o || !kv_len) return DCA_ERR_INVALID_ARG;
   if (B < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || Hq < 1 || Hkv < 1 || Hq % Hkv)
     return DCA_ERR_INVALID_ARG;
-  if (!cw_ok(c, w) || !base_ok(rope_base) || !isfinite(sm_scale)) return DCA_ERR_INVALID_ARG;
+  if ((dm.map == kMapDCA && !cw_ok(c, w)) || !base_ok(rope_base) || !isfinite(sm_scale)) return DCA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
     return DCA_ERR_INVALID_ARG;
+  if (dm.map != kMapDCA && (!dm.kc2 || !aligned(dm.kc2, 16))) return DCA_ERR_INVALID_ARG;
   int64_t max_kv = 0;
   for (int64_t b = 0; b < B; ++b) {
     if (kv_len[b] < 1 || kv_len[b] > cache_len) return DCA_ERR_INVALID_ARG;
     max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
   }
   DecodeLayout p;
-  if (!decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  std::vector<int64_t> seg;
+  if (!map_decode_layout(kv_len, B, Hq, Hkv, D, dtype, dm, &p, &seg)) return DCA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
   uint8_t* base = (uint8_t*)ws;
   const int64_t es = elem_size(dtype);
@@ -629,6 +672,14 @@ int decode_varlen_impl(const void* q, const void* k_cache, const void* v_cache, 
     a.cache_len = (int)cache_len;
     a.per_seq = 1;
     for (int i = 0; i < nb; ++i) a.seq_len[i] = (int)kv_len[b0 + i];
+    a.map = dm.map;
+    if (dm.map != kMapDCA) {
+      a.kc2 = (const uint8_t*)dm.kc2 + b0 * cache_len * Hkv * D * es;
+      for (int i = 0; i < nb; ++i) a.seg[i] = (int)seg[b0 + i];
+    }
+    a.se_group = dm.se_group;
+    a.se_window = dm.se_window;
+    a.cf_inv_kappa = dm.cf_inv_kappa;
     const hipError_t e = launch_decode(a, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return DCA_ERR_HIP;
   }
@@ -657,14 +708,8 @@ extern "C" {
 
 size_t dca_decode_varlen_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
                                          int64_t D, int dtype) {
-  if (!kv_len || B < 1 || B >= kMaxDim) return 0;
-  int64_t max_kv = 0;
-  for (int64_t b = 0; b < B; ++b) {
-    if (kv_len[b] < 1 || kv_len[b] >= kMaxDim / 2) return 0;
-    max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
-  }
   DecodeLayout p;
-  return decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+  return map_decode_layout(kv_len, B, Hq, Hkv, D, dtype, DecodeMap{}, &p, nullptr) ? p.total : 0;
 }
 
 int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -704,6 +749,75 @@ int dca_decode_paged(const void* q, const void* k_pages, const void* v_pages, co
   if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
   return decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, max_blocks * page_size, Hq, Hkv, D, c, w,
                             rope_base, sm_scale, dtype, ws, ws_bytes, stream, pg);
+}
+
+
+size_t dca_selfextend_decode_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                             int group, int window, int dtype) {
+  if (!se_ok(group, window)) return 0;
+  DecodeMap m;
+  m.map = kMapSelfExtend;
+  m.se_group = group;
+  m.se_window = window;
+  DecodeLayout p;
+  return map_decode_layout(kv_len, B, Hq, Hkv, D, dtype, m, &p, nullptr) ? p.total : 0;
+}
+
+int dca_selfextend_decode(const void* q, const void* k_cache, const void* k_cache_grouped, const void* v_cache,
+                          void* o, float* lse, const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq,
+                          int64_t Hkv, int64_t D, int group, int window, double rope_base, float sm_scale,
+                          int dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!se_ok(group, window) || !k_cache_grouped) return DCA_ERR_INVALID_ARG;
+  DecodeMap m;
+  m.map = kMapSelfExtend;
+  m.kc2 = k_cache_grouped;
+  m.se_group = group;
+  m.se_window = window;
+  const int unbounded = 1 << 30;   // no chunk relation: s never splits a range
+  return decode_varlen_impl(q, k_cache, v_cache, o, lse, kv_len, B, cache_len, Hq, Hkv, D, unbounded, 0,
+                            rope_base, sm_scale, dtype, ws, ws_bytes, stream, PagedKv{}, m);
+}
+
+size_t dca_coarse_fine_decode_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
+                                              int64_t D, int chunk, int dtype) {
+  if (chunk < 1 || chunk > (1 << 24)) return 0;
+  DecodeMap m;
+  m.map = kMapCoarseFine;
+  m.cf_chunk = chunk;
+  DecodeLayout p;
+  return map_decode_layout(kv_len, B, Hq, Hkv, D, dtype, m, &p, nullptr) ? p.total : 0;
+}
+
+int dca_coarse_fine_decode(const void* q, const void* k_cache, const void* k_cache_scaled, const void* v_cache,
+                           void* o, float* lse, const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq,
+                           int64_t Hkv, int64_t D, int chunk, int train_len, int target_len, double rope_base,
+                           float sm_scale, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (chunk < 1 || chunk > (1 << 24) || train_len < 1 || target_len < 1 || !k_cache_scaled)
+    return DCA_ERR_INVALID_ARG;
+  DecodeMap m;
+  m.map = kMapCoarseFine;
+  m.kc2 = k_cache_scaled;
+  m.cf_chunk = chunk;
+  m.cf_inv_kappa = (double)train_len / (double)target_len;
+  // the chunk relation uses chunk size C (held in c and s)
+  return decode_varlen_impl(q, k_cache, v_cache, o, lse, kv_len, B, cache_len, Hq, Hkv, D, chunk, 0, rope_base,
+                            sm_scale, dtype, ws, ws_bytes, stream, PagedKv{}, m);
+}
+
+int dca_coarse_fine_key_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D, int64_t pos0,
+                              int chunk, int train_len, int target_len, double rope_base, int dtype, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!x || !out || B < 0 || L < 0 || H < 0 || pos0 < 0) return DCA_ERR_INVALID_ARG;
+  if (B >= kMaxDim || L >= kMaxDim || H >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
+  if (chunk < 1 || chunk > (1 << 24) || train_len < 1 || target_len < 1 || !base_ok(rope_base))
+    return DCA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16)) return DCA_ERR_INVALID_ARG;
+  if (B == 0 || L == 0 || H == 0) return DCA_OK;
+  const double step = (double)chunk * (double)train_len / (double)target_len;
+  return hip_status(launch_rope_remap(x, out, B, L, H, D, pos0, kRemapCoarseScaled, chunk, 0, rope_base, dtype,
+                                      (hipStream_t)stream, step));
 }
 
 }  // extern "C"

@@ -24,10 +24,13 @@ hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st);
 hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
                                  hipStream_t st);
 
-// dca_rope_remap kernel (dtype 0 = fp32, 1 = bf16).
+// dca_rope_remap kernel (dtype 0 = fp32, 1 = bf16).  map kRemapCoarseScaled
+// (internal): the coarse / fine map's scaled key position, floor(p / c) *
+// step + p mod c with step = C / kappa (w unused).
+constexpr int kRemapCoarseScaled = 7;
 hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
                              int64_t pos0, int map, int c, int w, double base, int dtype,
-                             hipStream_t st);
+                             hipStream_t st, double step = 0.0);
 
 // Key rotation into head-major krot [B, Hkv, Lp, D] (+ optional BSHD copy):
 // key j is turned to position (j / kdiv) mod kmod (DCA: kdiv 1, kmod s;
@@ -132,13 +135,26 @@ struct DecodeArgs {
   // launcher).
   int wave_start[kMaxSeqGroup + 1];
   PagedKv pg;          // kc / vc are page pools (cache_len unused), or bt null
+  // Position map (PosMap).  SelfExtend and coarse / fine keep two key caches:
+  // keys j < seg[b] (grouped, resp. two or more chunks before the query's)
+  // are read from kc2, the others from kc; each segment is cut into ranges
+  // of keys_per_split keys on its own.  DCA: seg[b] = 0, kc2 unused.  The
+  // query variants: DCA intra / succ / inter; SelfExtend grouped /
+  // neighbor; coarse / fine intra / succ / inter at real positions.
+  int map;
+  const void* kc2;
+  int seg[kMaxSeqGroup];
+  int se_group, se_window;
+  double cf_inv_kappa;
 };
 
 // Split plan shared by the workspace queries and the launchers: kv holds the
 // B sequences' cached key counts (host memory), or is null for B sequences
 // of uniform_kv keys.
-void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv, int dtype,
-                 int* keys_per_split, int* nsplit);
+// seg: per-sequence segment boundaries (host memory, keys below are ranged
+// on their own), or null for one segment.
+void decode_plan(const int64_t* kv, const int64_t* seg, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv,
+                 int dtype, int* keys_per_split, int* nsplit);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
 
 }  // namespace dca

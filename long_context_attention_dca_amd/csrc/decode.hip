@@ -47,6 +47,26 @@ __device__ inline int swz(int row, int chunk) {
 // ---- 1. query variants -------------------------------------------------------------
 // The new token of sequence b sits at (its cached key count) - 1.
 __device__ inline int seq_keys(const DecodeArgs& a, int b) { return a.per_seq ? a.seq_len[b] : a.kv_len; }
+__host__ __device__ inline int seq_seg(const DecodeArgs& a, int b) { return a.per_seq ? a.seg[b] : 0; }
+// Key ranges of sequence b: ceil(seg / kps) over [0, seg), then
+// ceil((keys - seg) / kps) over [seg, keys).
+__host__ __device__ inline int seq_ranges(int keys, int seg, int kps) {
+  return (seg + kps - 1) / kps + (keys - seg + kps - 1) / kps;
+}
+// Key range `split` of sequence b: [kbeg, kend); second = read from kc2.
+__device__ inline void range_of(const DecodeArgs& a, int b, int split, int* kbeg, int* kend, bool* second) {
+  const int keys = seq_keys(a, b), seg = seq_seg(a, b), kps = a.keys_per_split;
+  const int n0 = (seg + kps - 1) / kps;
+  if (split < n0) {
+    *kbeg = split * kps;
+    *kend = min(*kbeg + kps, seg);
+    *second = true;
+  } else {
+    *kbeg = seg + (split - n0) * kps;
+    *kend = min(*kbeg + kps, keys);   // may be empty (ragged batch)
+    *second = false;
+  }
+}
 
 template <typename T>
 __global__ void decode_qprep_kernel(DecodeArgs a) {
@@ -62,8 +82,15 @@ __global__ void decode_qprep_kernel(DecodeArgs a) {
   const int r = qpos % s;
 #pragma unroll
   for (int cls = 0; cls < 3; ++cls) {
+    double pos;
+    if (a.map == kMapSelfExtend)   // variant 0 grouped, 1 neighbor (2 unused)
+      pos = cls == 0 ? (double)se_query_pos_grouped(qpos, a.se_group, a.se_window) : (double)qpos;
+    else if (a.map == kMapCoarseFine)
+      pos = cf_query_pos(cls, qpos, c, a.cf_inv_kappa);
+    else
+      pos = (double)query_pos(cls, r, s, c);
     double sn, cs;
-    sincos((double)query_pos(cls, r, s, c) * theta, &sn, &cs);
+    sincos(pos * theta, &sn, &cs);
     T* dst = qv + ((int64_t)bh * 3 + cls) * D;
     Elem<T>::store(dst + k, (float)(x1 * cs - x2 * sn));
     Elem<T>::store(dst + k + half, (float)(x2 * cs + x1 * sn));
@@ -118,15 +145,18 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   const bool qvalid = qi < G;
   const int hq = g * G + (qvalid ? qi : 0);
   const int kv_len = seq_keys(a, b), s = a.s;
-  const int kbeg = split * a.keys_per_split;
-  const int kend = min(kbeg + a.keys_per_split, kv_len);   // may be empty (ragged batch)
+  int kbeg, kend;
+  bool second;
+  range_of(a, b, split, &kbeg, &kend, &second);
   const int qpos = kv_len - 1;
   const int nq = qpos / s;
+  // SelfExtend: one relation per segment (grouped below seg, neighbor above)
+  const int seg_cls = second ? 0 : 1;
 
   uint8_t* kl = smem + wave * WBYTES;
   uint8_t* vl = kl + KBYTES;
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive cache rows
-  const uint16_t* kc = (const uint16_t*)a.kc + (int64_t)g * D;
+  const uint16_t* kc = (const uint16_t*)(second ? a.kc2 : a.kc) + (int64_t)g * D;
   const uint16_t* vc = (const uint16_t*)a.vc + (int64_t)g * D;
   const uint16_t* qv = (const uint16_t*)a.qv + ((int64_t)b * a.Hq + hq) * 3 * D;
 
@@ -248,7 +278,8 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
     __builtin_amdgcn_wave_barrier();
 
     const int jl = min(j0 + SUB, kend) - 1;
-    const int cls_lo = min(nq - jl / s, 2), cls_hi = min(nq - j0 / s, 2);
+    const bool se = a.map == kMapSelfExtend;
+    const int cls_lo = se ? seg_cls : min(nq - jl / s, 2), cls_hi = se ? seg_cls : min(nq - j0 / s, 2);
     const bool straddle = cls_lo != cls_hi;
     const bool tail = j0 + SUB > kend;
     // A sub-tile spanning several relations is processed once per relation
@@ -355,14 +386,15 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
   const int b = bh / a.Hq, hq = bh - b * a.Hq;
   const int G = a.Hq / a.Hkv, g = hq / G;
   const int kv_len = seq_keys(a, b), s = a.s;
-  const int kbeg = split * a.keys_per_split;
-  const int kend = min(kbeg + a.keys_per_split, kv_len);   // may be empty (ragged batch)
+  int kbeg, kend;
+  bool second;
+  range_of(a, b, split, &kbeg, &kend, &second);   // past the sequence's ranges: empty
   const int nq = (kv_len - 1) / s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float* qv = (const float*)a.qv + (int64_t)bh * 3 * D;
   for (int idx = tid; idx < 3 * D; idx += 256) qs[idx / D][idx % D] = qv[idx];
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const float* kc = (const float*)a.kc + (int64_t)g * D;
+  const float* kc = (const float*)(second ? a.kc2 : a.kc) + (int64_t)g * D;
   const float* vc = (const float*)a.vc + (int64_t)g * D;
   __shared__ int64_t rows[256];   // cache row of each key of the current step (-1: unreadable page)
   float m = -INFINITY, l = 0.f, o = 0.f;  // thread tid < D owns output dim tid
@@ -376,7 +408,7 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
       if (row < 0) {
         x = __builtin_nanf("");   // unreadable page: the row's result becomes NaN
       } else {
-        const int cls = min(nq - j / s, 2);
+        const int cls = a.map == kMapSelfExtend ? (second ? 0 : 1) : min(nq - j / s, 2);
         const float* kr = kc + row * row_stride;
         float acc = 0.f;
         for (int d = 0; d < D; ++d) acc = fmaf(qs[cls][d], kr[d], acc);
@@ -429,7 +461,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
   float* __restrict__ lse = a.lse;
   const int D = a.D;
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const int ns = (seq_keys(a, bh / a.Hq) + a.keys_per_split - 1) / a.keys_per_split;
+  const int ns = seq_ranges(seq_keys(a, bh / a.Hq), seq_seg(a, bh / a.Hq), a.keys_per_split);
   const float* pl = a.part_lse + (int64_t)bh * a.nsplit;
   float M = -INFINITY;
   for (int i = tid; i < ns; i += 128) M = fmaxf(M, pl[i]);
@@ -459,8 +491,8 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv, int dtype,
-                 int* keys_per_split, int* nsplit) {
+void decode_plan(const int64_t* kv, const int64_t* seg, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv,
+                 int dtype, int* keys_per_split, int* nsplit) {
   // One wave per key range, as many ranges as the chip holds at once: MI355X
   // runs 8 of these waves per CU (2 per SIMD) on 256 CUs.  The range length is
   // the shortest multiple of 32 keys whose ranges, over the whole batch (a
@@ -471,19 +503,25 @@ void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, i
   const int64_t waves_per_key = dtype == 0 ? Hq : Hkv * ((G + 31) / 32);  // waves reading one cached key
   const int64_t target = 2048;
   auto len = [&](int64_t b) { return kv ? kv[b] : uniform_kv; };
+  auto ranges = [&](int64_t b, int64_t kps) {
+    const int64_t n = len(b), sg = seg ? seg[b] : 0;
+    return (sg + kps - 1) / kps + (n - sg + kps - 1) / kps;
+  };
   int64_t max_kv = 0;
   for (int64_t b = 0; b < B; ++b) max_kv = len(b) > max_kv ? len(b) : max_kv;
   auto waves = [&](int64_t kps) {
     if (!kv) return B * ((uniform_kv + kps - 1) / kps) * waves_per_key;
     int64_t n = 0;
-    for (int64_t b = 0; b < B; ++b) n += (kv[b] + kps - 1) / kps;
+    for (int64_t b = 0; b < B; ++b) n += ranges(b, kps);
     return n * waves_per_key;
   };
   // Search in units of SUB keys.  At least 256 keys per range, and at most
   // kMaxSplits ranges per sequence (the combine kernel keeps one weight per
-  // range in LDS).  waves() never grows with the range length; if even one
-  // range per sequence overflows the round, the whole length is taken.
-  int64_t lo = (max_kv + kMaxSplits - 1) / kMaxSplits;
+  // range in LDS; a second segment can add one range).  waves() never grows
+  // with the range length; if even one range per segment overflows the
+  // round, the whole length is taken.
+  const int64_t cap = seg ? kMaxSplits - 1 : kMaxSplits;
+  int64_t lo = (max_kv + cap - 1) / cap;
   lo = (round_up(lo < 256 ? 256 : lo, SUB)) / SUB;
   int64_t hi = round_up(max_kv, SUB) / SUB;
   if (hi < lo) hi = lo;
@@ -496,7 +534,9 @@ void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, i
   }
   const int64_t kps = lo * SUB;
   *keys_per_split = (int)kps;
-  *nsplit = (int)((max_kv + kps - 1) / kps);
+  int64_t ns = 0;
+  for (int64_t b = 0; b < (kv ? B : 1); ++b) ns = ranges(b, kps) > ns ? ranges(b, kps) : ns;
+  *nsplit = (int)ns;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
@@ -514,8 +554,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
     if (a.per_seq) {   // flat numbering of the real ranges, sequence by sequence
       b.wave_start[0] = 0;
       for (int i = 0; i < a.B; ++i)
-        b.wave_start[i + 1] = b.wave_start[i] +
-                              (a.seq_len[i] + a.keys_per_split - 1) / a.keys_per_split * a.Hkv * nqg;
+        b.wave_start[i + 1] = b.wave_start[i] + seq_ranges(a.seq_len[i], a.seg[i], a.keys_per_split) * a.Hkv * nqg;
       waves = b.wave_start[a.B];
     }
     const dim3 grid((unsigned)((waves + 3) / 4));

@@ -83,15 +83,17 @@ template <typename T>
 __global__ void __launch_bounds__(256) rope_remap_kernel(const T* __restrict__ x, T* __restrict__ out,
                                                          int64_t B, int64_t L, int H, int D,
                                                          int64_t pos0, int map, int c, int w,
-                                                         double base) {
+                                                         double base, double step) {
   __shared__ double2 cs[64];
   const int64_t t = blockIdx.x;
   const int half = D / 2;
-  const int64_t P = remap_position(pos0 + t, map, c, w);
+  const int64_t p = pos0 + t;
+  const double P = map == kRemapCoarseScaled ? (double)(p / c) * step + (double)(p % c)
+                                             : (double)remap_position(p, map, c, w);
   if ((int)threadIdx.x < half) {
     const double theta = pow(base, -2.0 * (double)threadIdx.x / (double)D);
     double sn, cn;
-    sincos((double)P * theta, &sn, &cn);
+    sincos(P * theta, &sn, &cn);
     cs[threadIdx.x] = make_double2(cn, sn);
   }
   __syncthreads();
@@ -111,15 +113,15 @@ __global__ void __launch_bounds__(256) rope_remap_kernel(const T* __restrict__ x
 
 hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
                              int64_t pos0, int map, int c, int w, double base, int dtype,
-                             hipStream_t st) {
+                             hipStream_t st, double step) {
   if (L == 0 || B == 0 || H == 0) return hipSuccess;
   if (dtype == 0)
     hipLaunchKernelGGL(rope_remap_kernel<float>, dim3((unsigned)L), dim3(256), 0, st,
-                       (const float*)x, (float*)out, B, L, (int)H, (int)D, pos0, map, c, w, base);
+                       (const float*)x, (float*)out, B, L, (int)H, (int)D, pos0, map, c, w, base, step);
   else
     hipLaunchKernelGGL(rope_remap_kernel<uint16_t>, dim3((unsigned)L), dim3(256), 0, st,
                        (const uint16_t*)x, (uint16_t*)out, B, L, (int)H, (int)D, pos0, map, c, w,
-                       base);
+                       base, step);
   return hipGetLastError();
 }
 

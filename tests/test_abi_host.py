@@ -319,3 +319,42 @@ def test_prefill_chunk_paged_validation(lib):
     a = list(ok)
     a[7] = _i64s(0, 0)
     assert lib.dca_prefill_chunk_paged(*a) == 0
+
+
+def test_map_decode_workspace_and_validation(lib):
+    kv = _i64s(100, 3000, 777)
+    # a window covering every cache: one segment, the DCA ragged plan
+    assert lib.dca_selfextend_decode_workspace_bytes(kv, 3, 16, 2, 128, 4, 10 ** 6, 1) == \
+        lib.dca_decode_varlen_workspace_bytes(kv, 3, 16, 2, 128, 1)
+    # two segments: at least as many partials
+    assert lib.dca_selfextend_decode_workspace_bytes(kv, 3, 16, 2, 128, 4, 64, 1) >= \
+        lib.dca_decode_varlen_workspace_bytes(kv, 3, 16, 2, 128, 1)
+    assert lib.dca_coarse_fine_decode_workspace_bytes(kv, 3, 16, 2, 128, 64, 1) > 0
+    assert lib.dca_selfextend_decode_workspace_bytes(kv, 3, 16, 2, 128, 0, 64, 1) == 0     # group 0
+    assert lib.dca_coarse_fine_decode_workspace_bytes(kv, 3, 16, 2, 128, 0, 1) == 0        # chunk 0
+    assert lib.dca_coarse_fine_decode_workspace_bytes(_i64s(5, 0), 2, 16, 2, 128, 64, 1) == 0
+    # q, kc, kc2, vc, o, lse, kv_len, B, cache_len, Hq, Hkv, D, group, window, base, scale, dtype, ws, bytes, st
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(40, 100), 2, 128, 8, 2, 64, 4, 16, 1e4, 0.0, 1,
+          FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(2, None, -1), (12, 0, -1), (13, -1, -1), (6, _i64s(40, 129), -1), (11, 96, -2),
+                       (16, 5, -2), (18, 64, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_selfextend_decode(*a) == st, (i, bad)
+    # ..., chunk, train_len, target_len, base, scale, dtype, ws, bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(40, 100), 2, 128, 8, 2, 64, 64, 4, 32, 1e4, 0.0, 1,
+          FAKE_WS, 1 << 30, None]
+    for i, bad, st in [(2, None, -1), (12, 0, -1), (13, 0, -1), (14, 0, -1), (6, _i64s(0, 5), -1),
+                       (11, 80, -2), (19, 64, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_coarse_fine_decode(*a) == st, (i, bad)
+    # x, out, B, L, H, D, pos0, chunk, train, target, base, dtype, stream
+    ok = [FAKE, FAKE, 1, 10, 2, 64, 0, 16, 4, 32, 1e4, 1, None]
+    for i, bad, st in [(0, None, -1), (7, 0, -1), (8, 0, -1), (6, -1, -1), (5, 48, -2), (10, -1.0, -1)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_coarse_fine_key_remap(*a) == st, (i, bad)
+    a = list(ok)
+    a[3] = 0   # no rows: nothing to do
+    assert lib.dca_coarse_fine_key_remap(*a) == 0
