@@ -177,7 +177,8 @@ def main():
                                                 DC["seed"])
         dq = dq_h.to(dev)
         kraw = dk_h.to(dev)
-        del dk_h
+        if args.no_chunked:
+            del dk_h   # (kept for the SelfExtend / coarse-fine decode caches otherwise)
         kc = dca.rope_remap(kraw, dca.DCA_MAP_KEY, DC["c"], DC["w"], DC["base"], 0)
         del kraw
         vc = dv_h.to(dev)
@@ -334,6 +335,43 @@ def main():
                                        "frac": nbv / (pg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "page_size": PG,
                                        "kv_len": f"{kvr[0]}..{kvr[-1]} evenly spaced", "bytes_per_call": nbv}
         del pools, table, perm
+        torch.cuda.empty_cache()
+        # the same ragged batch under the SelfExtend (G 8, W 1024) and the
+        # guide's coarse / fine (C 512, 4096 -> 32768) maps: two rotated key
+        # caches each, built untimed
+        kraw = dk_h.to(dev)
+        del dk_h
+        plain = dca.rope_remap(kraw, dca.DCA_MAP_PLAIN, 1, 0, DC["base"], 0)
+        second = torch.empty_like(plain)
+        for key, build, call in (
+                ("selfextend_decode_100k",
+                 lambda: dca.rope_remap(kraw, dca.DCA_MAP_SE_KEY_GROUPED, 8, 1024, DC["base"], 0),
+                 lambda ws: dca.selfextend_decode(dq, plain, second, vc, kvr, 8, 1024, DC["base"], workspace=ws)),
+                ("coarse_fine_decode_100k",
+                 lambda: dca.coarse_fine_key_remap(kraw, 512, 4096, 32768, DC["base"]),
+                 lambda ws: dca.coarse_fine_decode(dq, plain, second, vc, kvr, 512, 4096, 32768, DC["base"],
+                                                   workspace=ws))):
+            second.copy_(build())
+            mbytes = (dca.selfextend_decode_workspace_bytes(kvr, DC["Hq"], DC["Hkv"], DC["D"], 8, 1024, torch.bfloat16)
+                      if "selfextend" in key else
+                      dca.coarse_fine_decode_workspace_bytes(kvr, DC["Hq"], DC["Hkv"], DC["D"], 512, torch.bfloat16))
+            mws = torch.empty(mbytes, dtype=torch.uint8, device=dev)
+            call(mws)
+            torch.cuda.synchronize()
+            mev = [events(2) for _ in range(nd)]
+            for i in range(nd):
+                mev[i][0].record()
+                call(mws)
+                mev[i][1].record()
+            torch.cuda.synchronize()
+            m_ms = sum(e[0].elapsed_time(e[1]) for e in mev) / nd
+            result[key] = {"ms": m_ms, "achieved": nbv / (m_ms * 1e-3) / 1e9, "unit": "GB/s",
+                           "frac": nbv / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                           "kv_len": f"{kvr[0]}..{kvr[-1]} evenly spaced", "bytes_per_call": nbv,
+                           "caches": "plain + " + ("grouped (G 8, W 1024)" if "selfextend" in key
+                                                   else "coarse-scaled (C 512, kappa 8)")}
+            del mws
+        del kraw, plain, second
         torch.cuda.empty_cache()
 
     # ---------------- SelfExtend 32k prefill (reported beside the step) ---------

@@ -389,6 +389,18 @@ def prefill_chunk_paged(q, k_pages, v_pages, block_table, pos0, c: int, w: int, 
     return (o, lse) if return_lse else o
 
 
+def selfextend_decode_workspace_bytes(kv_len, Hq, Hkv, D, group, window, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    kl, _ = _host_i64(kv_len, len(kv_len), "kv_len")
+    return int(_lib.load().dca_selfextend_decode_workspace_bytes(kl, len(kv_len), Hq, Hkv, D, group, window, code))
+
+
+def coarse_fine_decode_workspace_bytes(kv_len, Hq, Hkv, D, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    kl, _ = _host_i64(kv_len, len(kv_len), "kv_len")
+    return int(_lib.load().dca_coarse_fine_decode_workspace_bytes(kl, len(kv_len), Hq, Hkv, D, chunk, code))
+
+
 def _map_decode(fn_ws, fn, q, k_cache, k2, v_cache, kv_len, params, base, sm_scale, return_lse, workspace, name):
     lib = _lib.load()
     _check(q, "q", 3)

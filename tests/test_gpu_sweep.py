@@ -6,7 +6,7 @@ hundred (tile multiples and ragged tails alike), GQA ratios 1 / 2 / 4, both
 head dims, both dtypes, and the map parameters over their whole valid range
 (chunk sizes that straddle tiles, w = 0, windows wider than the sequence,
 group 1, chunk offsets that are and are not multiples of 32, page sizes
-16 / 32 / 48 / 64).  Inputs are the discriminating ones (q, k scaled by 2).
+16 / 32 / 48 / 64), and the SelfExtend and coarse / fine decodes.  Inputs are the discriminating ones (q, k scaled by 2).
 Bars: fp32 max-abs <= 1e-4; bf16 max-abs <= 2e-2 and mean-abs <= 2e-3.
 """
 import numpy as np
@@ -26,7 +26,7 @@ N_CASES = 24
 
 def _draw(kind, idx):
     rng = np.random.default_rng(10_000 + 97 * idx + {"dca": 0, "se": 1, "cf": 2, "chunk": 3, "dec": 4,
-                                                      "paged": 5}[kind])
+                                                      "paged": 5, "sedec": 6, "cfdec": 7}[kind])
     dtype = torch.bfloat16 if idx % 4 != 3 else torch.float32
     D = int(rng.choice([64, 128]))
     Hkv = int(rng.choice([1, 2]))
@@ -131,3 +131,47 @@ def test_sweep_paged_decode(idx):
     for b in range(B):
         Od, _ = oracle.dca_decode_ref(qd[b: b + 1], k[b: b + 1, : kv[b]], v[b: b + 1, : kv[b]], c, w)
         assert_close(o[b], Od[0], dtype, f"paged decode seq {b}")
+
+
+def _nan_tails(x, kv):
+    x = x.clone()
+    for b, n in enumerate(kv):
+        x[b, n:] = float("nan")
+    return x
+
+
+@pytest.mark.parametrize("idx", range(N_CASES))
+def test_sweep_selfextend_decode(idx):
+    rng, dtype, D, Hkv, G, B, L = _draw("sedec", idx)
+    B = int(rng.integers(1, 6))
+    grp = int(rng.integers(1, 9))
+    win = int(rng.choice([0, int(rng.integers(1, 1500)), 5000]))
+    kv = [int(rng.integers(1, 2500)) for _ in range(B)]
+    log(f"[sweep se decode] kv {kv} G{grp} W{win} Hq{Hkv * G} Hkv{Hkv} D{D} {dtype}")
+    qd, k, v = inputs.decode_inputs(B, max(kv), Hkv * G, Hkv, D, dtype, seed=600 + idx, qk_scale=2.0)
+    kg = k.to(dev())
+    kp = _nan_tails(dca.rope_remap(kg, dca.DCA_MAP_PLAIN, 1, 0), kv)
+    kq = _nan_tails(dca.rope_remap(kg, dca.DCA_MAP_SE_KEY_GROUPED, grp, win), kv)
+    o = to_np(dca.selfextend_decode(qd.to(dev()), kp, kq, _nan_tails(v.to(dev()), kv), kv, grp, win))
+    O, _ = oracle.selfextend_decode_ref(qd, k, v, kv, grp, win)
+    for b in range(B):
+        assert_close(o[b], O[b], dtype, f"selfextend decode seq {b}")
+
+
+@pytest.mark.parametrize("idx", range(N_CASES))
+def test_sweep_coarse_fine_decode(idx):
+    rng, dtype, D, Hkv, G, B, L = _draw("cfdec", idx)
+    B = int(rng.integers(1, 6))
+    chunk = int(rng.integers(1, 700))
+    train = int(rng.integers(1, 50))
+    target = int(rng.integers(train, 8 * train + 1))
+    kv = [int(rng.integers(1, 2500)) for _ in range(B)]
+    log(f"[sweep cf decode] kv {kv} C{chunk} {train}->{target} Hq{Hkv * G} Hkv{Hkv} D{D} {dtype}")
+    qd, k, v = inputs.decode_inputs(B, max(kv), Hkv * G, Hkv, D, dtype, seed=700 + idx, qk_scale=2.0)
+    kg = k.to(dev())
+    kp = _nan_tails(dca.rope_remap(kg, dca.DCA_MAP_PLAIN, 1, 0), kv)
+    ks = _nan_tails(dca.coarse_fine_key_remap(kg, chunk, train, target), kv)
+    o = to_np(dca.coarse_fine_decode(qd.to(dev()), kp, ks, _nan_tails(v.to(dev()), kv), kv, chunk, train, target))
+    O, _ = oracle.coarse_fine_decode_ref(qd, k, v, kv, chunk, train, target)
+    for b in range(B):
+        assert_close(o[b], O[b], dtype, f"coarse/fine decode seq {b}")
