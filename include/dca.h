@@ -87,13 +87,14 @@ int dca_version(void);
  * to.  DCA_MAP_KEY is how a decode KV cache is built; the query maps expose
  * the three query variants the attention kernels form internally.
  *
- *   x, out : [B, L, H, D] of `dtype`, device; out may equal x (in place).
+ *   x, out : [B, L, H, D] of `dtype`, device, 16-byte aligned; out may equal
+ *            x (in place).  B, L and H * D are each below 2^31.
  *   pos0   : >= 0, position of token 0.
  *   map    : one of DCA_MAP_*.  For DCA_MAP_SE_KEY_GROUPED / DCA_MAP_SE_Q_GROUPED
  *            c is the SelfExtend group size G (1 <= G <= 2^24) and w the
  *            window W (0 <= W <= 2^30); the DCA rule w < c does not apply.
  * Angles, cos/sin and the rotation are evaluated in fp64; the result is
- * rounded to nearest even into the output type (bf16 through fp32).
+ * rounded once, to nearest even, into the output type.
  */
 int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
                    int64_t pos0, int map, int c, int w, double rope_base, int dtype,
@@ -378,7 +379,8 @@ int dca_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pa
  *
  * dca_coarse_fine_key_remap: x [B, L, H, D] at positions pos0 .. pos0 + L - 1
  * rotated at the coarse-scaled key positions (fp64 angles, one rounding),
- * written to out (may alias x only if identical).
+ * written to out (may alias x only if identical); 16-byte aligned, with B,
+ * L and H * D each below 2^31.
  */
 size_t dca_selfextend_decode_workspace_bytes(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv,
                                              int64_t D, int group, int window, int dtype);

@@ -128,7 +128,7 @@ int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, in
                    int map, int c, int w, double rope_base, int dtype, void* stream) {
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!x || !out || B < 0 || L < 0 || H < 0 || pos0 < 0) return DCA_ERR_INVALID_ARG;
-  if (B >= kMaxDim || L >= kMaxDim || H >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
+  if (B >= kMaxDim || L >= kMaxDim || H * D >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
   const bool se_map = map == DCA_MAP_SE_KEY_GROUPED || map == DCA_MAP_SE_Q_GROUPED;
   if (map < DCA_MAP_KEY || map > DCA_MAP_SE_Q_GROUPED || !base_ok(rope_base)) return DCA_ERR_INVALID_ARG;
   if (se_map ? !se_ok(c, w) : !cw_ok(c, w)) return DCA_ERR_INVALID_ARG;
@@ -810,7 +810,7 @@ int dca_coarse_fine_key_remap(const void* x, void* out, int64_t B, int64_t L, in
                               int chunk, int train_len, int target_len, double rope_base, int dtype, void* stream) {
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!x || !out || B < 0 || L < 0 || H < 0 || pos0 < 0) return DCA_ERR_INVALID_ARG;
-  if (B >= kMaxDim || L >= kMaxDim || H >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
+  if (B >= kMaxDim || L >= kMaxDim || H * D >= kMaxDim || pos0 > (int64_t(1) << 52)) return DCA_ERR_INVALID_ARG;
   if (chunk < 1 || chunk > (1 << 24) || train_len < 1 || target_len < 1 || !base_ok(rope_base))
     return DCA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(out, 16)) return DCA_ERR_INVALID_ARG;

@@ -54,8 +54,9 @@ hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_k
 }
 
 // ---- dca_rope_remap -----------------------------------------------------------------
-// One workgroup per token t: the 64 (or 32) angles of its position are made
-// once in fp64 and applied to every (batch, head) row of that token.
+// One workgroup per kRemapTokens consecutive tokens: the angles of their
+// positions are made once in fp64 (one (token, k) pair per thread) and applied
+// to every (batch, head) row of those tokens, 16 bytes per load and store.
 // Maps 0-4 take the DCA (c, w); the SelfExtend maps 5 and 6 take c = G and
 // w = W.
 __device__ inline int64_t remap_position(int64_t p, int map, int c, int w) {
@@ -79,36 +80,117 @@ __device__ inline int64_t remap_position(int64_t p, int map, int c, int w) {
   }
 }
 
+// 16 bytes of T: 8 bf16 or 4 fp32 values, widened to float.
 template <typename T>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const uint4& u, float* f) { unpack_bf16x8(u, f); }
+  __device__ static uint4 pack(const float* f) { return pack_bf16x8(f); }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+// fp64 -> fp32 rounded to odd (round to nearest, then the odd neighbour when
+// that was inexact).  The 16 bits fp32 holds beyond bf16 keep the later
+// rounding to bf16 exact, so fp64 -> bf16 is rounded once, to nearest even,
+// whatever the compiler makes of the two conversions.
+__device__ inline float f32_round_odd(double d) {
+  const float f = (float)d;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != d && (u & 1u) == 0) u += fabs(d) > fabs(back) ? 1u : 0xffffffffu;
+  return __uint_as_float(u);
+}
+
+// Turn the pairs (x1[e], x2[e]) by the angles cs[e] = (cos, sin): fp64
+// arithmetic with the fma written out, so every caller computes the same
+// fp64 values, then the value handed back for T's single rounding.
+template <typename T, int N>
+__device__ inline void rotate_pairs(float* x1, float* x2, const double2* cs) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const double a = x1[e], b = x2[e];
+    const double y1 = fma(a, cs[e].x, -(b * cs[e].y));
+    const double y2 = fma(b, cs[e].x, a * cs[e].y);
+    if constexpr (sizeof(T) == 2) {
+      x1[e] = f32_round_odd(y1);
+      x2[e] = f32_round_odd(y2);
+    } else {
+      x1[e] = (float)y1;
+      x2[e] = (float)y2;
+    }
+  }
+}
+
+constexpr int kRemapTokens = 4;
+
+template <typename T, int D>
 __global__ void __launch_bounds__(256) rope_remap_kernel(const T* __restrict__ x, T* __restrict__ out,
-                                                         int64_t B, int64_t L, int H, int D,
-                                                         int64_t pos0, int map, int c, int w,
-                                                         double base, double step) {
-  __shared__ double2 cs[64];
-  const int64_t t = blockIdx.x;
-  const int half = D / 2;
-  const int64_t p = pos0 + t;
-  const double P = map == kRemapCoarseScaled ? (double)(p / c) * step + (double)(p % c)
-                                             : (double)remap_position(p, map, c, w);
-  if ((int)threadIdx.x < half) {
-    const double theta = pow(base, -2.0 * (double)threadIdx.x / (double)D);
+                                                         int64_t B, int64_t L, int H, int64_t pos0, int map,
+                                                         int c, int w, double base, double step) {
+  constexpr int half = D / 2, N = Vec16<T>::N, NG = half / N;   // 16-byte groups per half row
+  __shared__ double2 cs[kRemapTokens][half];
+  const int64_t t0 = (int64_t)blockIdx.x * kRemapTokens;
+  const int ntok = (int)(L - t0 < kRemapTokens ? L - t0 : kRemapTokens);
+  for (int idx = threadIdx.x; idx < ntok * half; idx += 256) {
+    const int tk = idx / half, k = idx - tk * half;
+    const int64_t p = pos0 + t0 + tk;
+    const double P = map == kRemapCoarseScaled ? (double)(p / c) * step + (double)(p % c)
+                                               : (double)remap_position(p, map, c, w);
+    const double theta = pow(base, -2.0 * (double)k / (double)D);
     double sn, cn;
     sincos(P * theta, &sn, &cn);
-    cs[threadIdx.x] = make_double2(cn, sn);
+    cs[tk][k] = make_double2(cn, sn);
   }
   __syncthreads();
-  const int64_t per_b = (int64_t)H * half;
-  for (int64_t idx = threadIdx.x; idx < B * per_b; idx += blockDim.x) {
-    const int64_t b = idx / per_b;
-    const int rem = (int)(idx - b * per_b);
-    const int h = rem / half, k = rem - h * half;
-    const int64_t off = ((b * L + t) * H + h) * D;
-    const double x1 = Elem<T>::load(x + off + k);
-    const double x2 = Elem<T>::load(x + off + k + half);
-    const double2 a = cs[k];
-    Elem<T>::store(out + off + k, (float)(x1 * a.x - x2 * a.y));
-    Elem<T>::store(out + off + k + half, (float)(x2 * a.x + x1 * a.y));
+  // Items (b, token, head, group) with the group fastest: a sequence's rows of
+  // these tokens are one contiguous run.  The batch index advances by
+  // subtraction, so no 64-bit division is made per item.
+  const int inner = ntok * H * NG;
+  int64_t b = threadIdx.x / inner;
+  int r = threadIdx.x - (int)b * inner;
+  const int step_b = 256 / inner, step_r = 256 - step_b * inner;
+  for (; b < B;) {
+    const int g = r % NG, th = r / NG, h = th % H, tk = th / H;
+    const int64_t off = ((b * L + t0 + tk) * H + h) * D + g * N;
+    float x1[N], x2[N];
+    Vec16<T>::unpack(*(const uint4*)(x + off), x1);
+    Vec16<T>::unpack(*(const uint4*)(x + off + half), x2);
+    rotate_pairs<T, N>(x1, x2, &cs[tk][g * N]);
+    *(uint4*)(out + off) = Vec16<T>::pack(x1);
+    *(uint4*)(out + off + half) = Vec16<T>::pack(x2);
+    b += step_b;
+    r += step_r;
+    if (r >= inner) {
+      r -= inner;
+      ++b;
+    }
   }
+}
+
+template <typename T>
+static void launch_remap_t(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D, int64_t pos0,
+                           int map, int c, int w, double base, hipStream_t st, double step) {
+  const dim3 grid((unsigned)((L + kRemapTokens - 1) / kRemapTokens));
+  if (D == 64)
+    hipLaunchKernelGGL((rope_remap_kernel<T, 64>), grid, dim3(256), 0, st, (const T*)x, (T*)out, B, L, (int)H,
+                       pos0, map, c, w, base, step);
+  else
+    hipLaunchKernelGGL((rope_remap_kernel<T, 128>), grid, dim3(256), 0, st, (const T*)x, (T*)out, B, L, (int)H,
+                       pos0, map, c, w, base, step);
 }
 
 hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D,
@@ -116,12 +198,9 @@ hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int
                              hipStream_t st, double step) {
   if (L == 0 || B == 0 || H == 0) return hipSuccess;
   if (dtype == 0)
-    hipLaunchKernelGGL(rope_remap_kernel<float>, dim3((unsigned)L), dim3(256), 0, st,
-                       (const float*)x, (float*)out, B, L, (int)H, (int)D, pos0, map, c, w, base, step);
+    launch_remap_t<float>(x, out, B, L, H, D, pos0, map, c, w, base, st, step);
   else
-    hipLaunchKernelGGL(rope_remap_kernel<uint16_t>, dim3((unsigned)L), dim3(256), 0, st,
-                       (const uint16_t*)x, (uint16_t*)out, B, L, (int)H, (int)D, pos0, map, c, w,
-                       base, step);
+    launch_remap_t<uint16_t>(x, out, B, L, H, D, pos0, map, c, w, base, st, step);
   return hipGetLastError();
 }
 
@@ -132,8 +211,10 @@ hipError_t launch_rope_remap(const void* x, void* out, int64_t B, int64_t L, int
 // 32x32 MFMA output layout, so the PV step reads 8 contiguous keys per lane.
 __device__ inline int vt_perm(int p) { return (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
-template <typename T, int D, bool TRANSPOSE_V>
-__global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
+// fp32 prepare pass (keys only; the fp32 kernels read V as it is): one
+// workgroup per (64-key tile, KV head, sequence), one rotary pair per thread.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
   constexpr int half = D / 2;
   constexpr int TK = kPrefillTileKeys;
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -160,8 +241,8 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
                               ? rope_cs((double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk),
                                         a.theta[kk])
                               : a.table[((j / a.kdiv) % a.kmod) * half + kk];
-        const float y1 = (float)(x1 * c.x - x2 * c.y);
-        const float y2 = (float)(x2 * c.x + x1 * c.y);
+        const float y1 = (float)fma(x1, c.x, -(x2 * c.y));   // as rotate_pairs<float>
+        const float y2 = (float)fma(x2, c.x, x1 * c.y);
         Elem<T>::store(dst + kk, y1);
         Elem<T>::store(dst + kk + half, y2);
         if (k_rot_out) {
@@ -177,38 +258,157 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepArgs a) {
       Elem<T>::store(dst + kk + half, 0.f);
     }
   }
-  if constexpr (TRANSPOSE_V) {
-    if (a.vt == nullptr) return;   // uniform: a second key rotation without V
-    __shared__ uint16_t vs[TK][D + 2];
-    const uint16_t* vv = reinterpret_cast<const uint16_t*>(a.v);
-    for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
-      const int row = idx / D, d = idx - row * D;
+}
+
+// bf16 prepare pass with 16-byte accesses throughout.  One workgroup per
+// (64-key tile, group of up to kPrepHeads KV heads, sequence).  A thread owns
+// (key row, 8-dim group) items: it gets the item's cos/sin once and applies
+// them to every head of the group.  The V rows of all the group's heads are
+// loaded before the key work, so their loads are in flight meanwhile, then
+// each head's tile is transposed through LDS and written as whole 16-byte
+// runs of 8 keys (in the key order of vt_perm).
+constexpr int kPrepHeads = 4;
+
+template <int D>
+__global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
+  constexpr int half = D / 2, NG = half / 8;             // 8-dim groups per half row
+  constexpr int TK = kPrefillTileKeys;
+  constexpr int KITEMS = TK * NG / 256;                  // key items per thread
+  constexpr int VG = D / 8;                              // 8-dim groups per V row
+  constexpr int VITEMS = TK * VG / 256;                  // V loads per thread and head
+  constexpr int OITEMS = D * (TK / 8) / 256;             // V^T stores per thread and head
+  static_assert(KITEMS >= 1 && VITEMS >= 1 && OITEMS >= 1, "tile too small for the workgroup");
+  const int tile = blockIdx.x, b = blockIdx.z, h0 = blockIdx.y * kPrepHeads;
+  const int nh = a.Hkv - h0 < kPrepHeads ? a.Hkv - h0 : kPrepHeads;
+  const int j0 = tile * TK;
+  const int Lb = a.per_seq ? a.seq_len[b] : a.L;   // valid rows of this sequence
+  const uint16_t* k = (const uint16_t*)a.k;
+  const uint16_t* vv = (const uint16_t*)a.v;
+  const bool with_v = a.vt != nullptr;
+  const bool rotate = a.table != nullptr || a.pos_mode == 1;
+
+  // V rows of every head of the group (zero past the valid rows and for
+  // unreadable pages).
+  uint4 vr[kPrepHeads][VITEMS];
+  if (with_v) {
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int item = threadIdx.x + it * 256;
+      const int row = item / VG, dg = item - row * VG;
       const int j = j0 + row;
       const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : -1;
-      vs[row][d] = crow >= 0 ? vv[(crow * a.Hkv + g) * D + d] : (uint16_t)0;
+#pragma unroll
+      for (int hh = 0; hh < kPrepHeads; ++hh)
+        vr[hh][it] = (hh < nh && crow >= 0) ? *(const uint4*)(vv + (crow * a.Hkv + h0 + hh) * D + dg * 8)
+                                            : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Keys.
+#pragma unroll
+  for (int it = 0; it < KITEMS; ++it) {
+    const int item = threadIdx.x + it * 256;
+    const int row = item / NG, kg = item - row * NG;
+    const int j = j0 + row, k0 = kg * 8;
+    const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : 0;
+    const bool valid = j < Lb && crow >= 0;
+    uint4 x1[kPrepHeads], x2[kPrepHeads];
+#pragma unroll
+    for (int hh = 0; hh < kPrepHeads; ++hh)
+      if (hh < nh && valid) {
+        const uint16_t* src = k + (crow * a.Hkv + h0 + hh) * D + k0;
+        x1[hh] = *(const uint4*)src;
+        x2[hh] = *(const uint4*)(src + half);
+      }
+    double2 cs[8];
+    if (valid && rotate) {
+      if (a.pos_mode == 1) {
+        const double pos = (double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = rope_cs(pos, a.theta[k0 + e]);
+      } else {
+        const double2* t = a.table + (int64_t)((j / a.kdiv) % a.kmod) * half + k0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = t[e];
+      }
+    }
+    const uint32_t nan2 = 0x7fc07fc0u;   // two bf16 quiet NaNs
+#pragma unroll
+    for (int hh = 0; hh < kPrepHeads; ++hh) {
+      if (hh >= nh) continue;
+      uint16_t* dst = (uint16_t*)a.krot + (((int64_t)b * a.Hkv + h0 + hh) * a.Lp + j) * D + k0;
+      uint4 y1, y2;
+      if (j >= Lb) {
+        y1 = y2 = make_uint4(0, 0, 0, 0);
+      } else if (crow < 0) {   // unreadable page: poison the key so the rows using it give NaN
+        y1 = y2 = make_uint4(nan2, nan2, nan2, nan2);
+      } else if (rotate) {
+        float f1[8], f2[8];
+        unpack_bf16x8(x1[hh], f1);
+        unpack_bf16x8(x2[hh], f2);
+        rotate_pairs<uint16_t, 8>(f1, f2, cs);
+        y1 = pack_bf16x8(f1);
+        y2 = pack_bf16x8(f2);
+        if (a.k_rot_out) {
+          uint16_t* ko = (uint16_t*)a.k_rot_out + (crow * a.Hkv + h0 + hh) * D + k0;
+          *(uint4*)ko = y1;
+          *(uint4*)(ko + half) = y2;
+        }
+      } else {   // already rotated: exact copy
+        y1 = x1[hh];
+        y2 = x2[hh];
+      }
+      *(uint4*)dst = y1;
+      *(uint4*)(dst + half) = y2;
+    }
+  }
+
+  // V^T tiles, one head at a time through LDS.
+  if (!with_v) return;
+  __shared__ __attribute__((aligned(16))) uint16_t vs[TK][D + 8];
+  const int ntiles = a.Lp / TK;
+  for (int hh = 0; hh < nh; ++hh) {
+    if (hh > 0) __syncthreads();   // the previous head's reads are done
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int item = threadIdx.x + it * 256;
+      const int row = item / VG, dg = item - row * VG;
+      uint4 u = vr[0][it];
+#pragma unroll
+      for (int x = 1; x < kPrepHeads; ++x)
+        if (x == hh) u = vr[x][it];
+      *(uint4*)&vs[row][dg * 8] = u;
     }
     __syncthreads();
-    const int ntiles = a.Lp / TK;
-    uint16_t* dst = (uint16_t*)a.vt + ((bg * ntiles + tile) * D) * TK;
-    for (int idx = threadIdx.x; idx < D * TK; idx += 256) {
-      const int d = idx / TK, p = idx - d * TK;
-      dst[idx] = vs[vt_perm(p)][d];
+    uint16_t* dst = (uint16_t*)a.vt + ((((int64_t)b * a.Hkv + h0 + hh) * ntiles + tile) * D) * TK;
+#pragma unroll
+    for (int it = 0; it < OITEMS; ++it) {
+      const int item = threadIdx.x + it * 256;
+      const int d = item / (TK / 8), kg = item - d * (TK / 8);
+      uint16_t e[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) e[x] = vs[vt_perm(kg * 8 + x)][d];
+      *(uint4*)(dst + d * TK + kg * 8) =
+          make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                     e[6] | ((uint32_t)e[7] << 16));
     }
   }
 }
 
 hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st) {
-  const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)a.Hkv, (unsigned)a.B);
   if (dtype == 0) {
+    const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)a.Hkv, (unsigned)a.B);
     if (a.D == 64)
-      hipLaunchKernelGGL((kv_prep_kernel<float, 64, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_prep_f32_kernel<float, 64>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((kv_prep_kernel<float, 128, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_prep_f32_kernel<float, 128>), grid, dim3(256), 0, st, a);
   } else {
+    const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)((a.Hkv + kPrepHeads - 1) / kPrepHeads),
+                    (unsigned)a.B);
     if (a.D == 64)
-      hipLaunchKernelGGL((kv_prep_kernel<uint16_t, 64, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_prep_bf16_kernel<64>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((kv_prep_kernel<uint16_t, 128, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_prep_bf16_kernel<128>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -145,6 +145,8 @@ def test_prefill_full_parity(case):
         assert err.max() <= 1e-6
     else:
         assert np.all(err <= bf16_ulp(Kr) + 1e-30)
+    # the prepare pass and dca_rope_remap round every key alike
+    assert torch.equal(krot, dca.rope_remap(k.to(dev()), dca.DCA_MAP_KEY, c, w, 1e4))
 
 
 def _mutant_succ_as_inter(monkeypatch):
