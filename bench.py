@@ -15,6 +15,7 @@ Printed JSON (one line, stdout):
   ms_per_step  wall time of one step (prefill + decode), timed region / K
   roofline     the attention kernel against the bf16 dense MFMA peak
   decode       decode GB/s against the HBM peak
+  rope_remap_100k  dca_rope_remap building the decode_100k key cache (GB/s)
   prefill_128k the same prefill at 131072 tokens
   cpu_baseline the fp64 oracle timed on a bounded sample of rows on the host
 """
@@ -60,9 +61,9 @@ def source_hash(files):
 
 
 def measured_traffic(key):
-    """HBM bytes per launch of kernel `key` ("prefill_attend" or "decode_split")
-    from the committed rocprofv3 counter runs, or None when that kernel's source
-    changed since they were taken."""
+    """HBM bytes per launch of kernel `key` ("prefill_attend", "prefill_prepare",
+    "decode_split" or "rope_remap") from the committed rocprofv3 counter runs,
+    or None when that kernel's source changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[key]
@@ -180,6 +181,15 @@ def main():
         if args.no_chunked:
             del dk_h   # (kept for the SelfExtend / coarse-fine decode caches otherwise)
         kc = dca.rope_remap(kraw, dca.DCA_MAP_KEY, DC["c"], DC["w"], DC["base"], 0)
+        # the cache build itself (dca_rope_remap at DCA_MAP_KEY), timed on its own
+        torch.cuda.synchronize()
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for e in rev:
+            e[0].record()
+            dca.rope_remap(kraw, dca.DCA_MAP_KEY, DC["c"], DC["w"], DC["base"], 0, out=kc)
+            e[1].record()
+        torch.cuda.synchronize()
+        remap_ms = sum(e[0].elapsed_time(e[1]) for e in rev) / len(rev)
         del kraw
         vc = dv_h.to(dev)
         del dv_h
@@ -238,9 +248,15 @@ def main():
                               "kernel": prefill_kernel_name(P["c"], P["w"], P["D"]),
                               "kernel_ms": att_ms, "flops_per_launch": fl}
         att_all = sorted(e[1].elapsed_time(e[2]) for e in pe)
+        # the prepare pass reads K and V once and writes the rotated keys and
+        # the V tiles once (HBM-bound)
+        prep_bytes = 4 * P["B"] * P["L"] * P["Hkv"] * P["D"] * 2
         result["prefill_32k"] = {"ms": prep_ms + att_ms, "prepare_ms": prep_ms, "attend_ms": att_ms,
                                  "attend_ms_median": att_all[len(att_all) // 2], "attend_ms_min": att_all[0],
-                                 "tflops": result["value"]}
+                                 "tflops": result["value"],
+                                 "prepare_gbps": prep_bytes / (prep_ms * 1e-3) / 1e9,
+                                 "prepare_frac": prep_bytes / (prep_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                 "prepare_bytes": prep_bytes, "prepare_traffic": measured_traffic("prefill_prepare")}
     if run_decode:
         dec_ms = sum(e[0].elapsed_time(e[1]) for e in de) / args.steps
         nb = decode_bytes(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"])
@@ -252,6 +268,11 @@ def main():
                             "traffic": measured_traffic("decode_split")}
         if not run_prefill:
             result["value"], result["unit"] = gbps, "GB/s"
+        rb = 2 * DC["B"] * DC["kv_len"] * DC["Hkv"] * DC["D"] * 2   # read and write once
+        result["rope_remap_100k"] = {"ms": remap_ms, "achieved": rb / (remap_ms * 1e-3) / 1e9, "unit": "GB/s",
+                                     "frac": rb / (remap_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bytes_per_call": rb,
+                                     "bound": "hbm", "traffic": measured_traffic("rope_remap"),
+                                     "includes": "the decode_100k key cache built at j mod s"}
     cfg = {"workload": "llama2_70b_32k prefill + decode_100k" if run_prefill and run_decode else
            ("llama2_70b_32k prefill" if run_prefill else "decode_100k"),
            "prefill": {k_: P[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")},
