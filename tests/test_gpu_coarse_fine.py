@@ -36,6 +36,8 @@ CF_SMALL = [
     # any one wave's relation
     ("bf16_c64_l128_mixed_workgroup", 1, 128, 1, 1, 128, 64, 1, 8, torch.bfloat16, 2.0),
     ("bf16_c128_three_relations_one_wg", 1, 600, 2, 1, 64, 128, 1, 8, torch.bfloat16, 2.0),
+    # five KV heads: the prepare pass's second 4-head group holds one
+    ("bf16_hkv5", 1, 300, 10, 5, 128, 64, 2, 9, torch.bfloat16, 2.0),
 ]
 
 

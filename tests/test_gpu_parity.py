@@ -101,6 +101,21 @@ def test_rope_remap_all_maps(dtype, D, pos0):
     assert torch.equal(y, dca.rope_remap(xg, dca.DCA_MAP_KEY, c, w, 1e4, pos0))
 
 
+@pytest.mark.parametrize("B,L,H", [(17, 5, 64), (1, 1, 1), (3, 9, 2), (2, 130, 40)])
+def test_rope_remap_shapes(B, L, H):
+    # token counts that are not multiples of the 4 tokens a workgroup takes,
+    # head counts whose rows exceed one pass of the workgroup, batch > 16
+    for dtype, D in ((torch.bfloat16, 128), (torch.float32, 64)):
+        x = inputs.prefill_inputs(B, L, H, H, D, dtype, seed=15, qk_scale=1.0)[0]
+        got = to_np(dca.rope_remap(x.to(dev()), dca.DCA_MAP_KEY, 96, 32, 1e4, 41))
+        want = oracle.rope_remap_ref(x, 41, oracle.MAP_KEY, 96, 32, 1e4)
+        err = np.abs(got - want)
+        if dtype == torch.float32:
+            assert err.max() <= 1e-6, (B, L, H, err.max())
+        else:
+            assert np.all(err <= bf16_ulp(want) + 1e-30), (B, L, H, err.max())
+
+
 # ----------------------------------------------------- prefill, small -------
 SMALL = [
     # name, B, L, Hq, Hkv, D, c, w, dtype, qk_scale
@@ -124,6 +139,10 @@ SMALL = [
     ("bf16_s64_L1", 1, 1, 2, 1, 128, 64, 0, torch.bfloat16, 2.0),
     ("bf16_s64_L300", 1, 300, 2, 2, 128, 100, 36, torch.bfloat16, 2.0),
     ("bf16_s256_L257", 3, 257, 2, 1, 64, 320, 64, torch.bfloat16, 2.0),
+    # KV head counts that leave the prepare pass's last 4-head group partly empty
+    ("bf16_hkv6_gqa2", 1, 400, 12, 6, 128, 192, 64, torch.bfloat16, 2.0),
+    ("bf16_hkv5_mha_d64", 2, 250, 5, 5, 64, 128, 0, torch.bfloat16, 2.0),
+    ("bf16_hkv3_s_straddle", 1, 300, 6, 3, 128, 100, 4, torch.bfloat16, 2.0),
 ]
 
 
