@@ -28,6 +28,9 @@
  *     all accumulation are fp32.  Head dim D must be 64 or 128.
  *   - GQA: Hq must be a multiple of Hkv; query head h reads KV head
  *     floor(h * Hkv / Hq) (contiguous groups).
+ *   - Size limits: B, Hq and Hkv at most 65535 for the prefill entry points
+ *     (Hq below 65536 for decode), sequence lengths below 2^30; a call
+ *     outside them returns DCA_ERR_INVALID_ARG (the size queries return 0).
  *   - stream is a hipStream_t (NULL = the null stream).  Calls are
  *     asynchronous: a return of DCA_OK means "enqueued".  Device faults surface
  *     at the caller's next synchronisation.

@@ -51,12 +51,26 @@ def test_status_strings_and_version(lib):
 def test_prefill_workspace_sizes(lib):
     # fp32, B=1, L=512, Hkv=1, D=64, c=128: fp64 table 128*32*16 B, rotated keys 512*64*4 B.
     assert lib.dca_prefill_workspace_bytes(1, 512, 1, 64, 128, 0) == 128 * 32 * 16 + 2 * 512 * 64 * 4
-    # plus the values (bf16: tiled transpose); L is padded to a multiple of 64 rows.
+    # plus the values (bf16: tiled transpose); L is padded to a multiple of 128 rows.
     n = lib.dca_prefill_workspace_bytes(2, 100, 3, 128, 4096, 1)
     assert n == 4096 * 64 * 16 + 2 * (2 * 3 * 128 * 128 * 2)
     for bad in [(0, 512, 1, 64, 128, 0), (1, 0, 1, 64, 128, 0), (1, 512, 1, 96, 128, 0),
                 (1, 512, 1, 64, 128, 7), (1, 512, 0, 64, 128, 1)]:
         assert lib.dca_prefill_workspace_bytes(*bad) == 0
+
+
+def test_prefill_family_size_limits(lib):
+    # B and Hkv index grid dimensions (at most 65535); beyond, every size query
+    # of the prefill family returns 0 instead of a size the launch cannot use
+    assert lib.dca_prefill_workspace_bytes(65535, 1, 1, 64, 128, 1) > 0
+    assert lib.dca_prefill_workspace_bytes(65536, 1, 1, 64, 128, 1) == 0
+    assert lib.dca_prefill_workspace_bytes(1, 1, 65536, 64, 128, 1) == 0
+    assert lib.dca_selfextend_workspace_bytes(65536, 10, 1, 64, 4, 8, 1) == 0
+    assert lib.dca_selfextend_workspace_bytes(65535, 10, 1, 64, 4, 8, 1) > 0
+    assert lib.dca_coarse_fine_workspace_bytes(1, 10, 65536, 64, 1) == 0
+    assert lib.dca_coarse_fine_workspace_bytes(1, 10, 65535, 64, 1) > 0
+    # a padded key copy past 2^56 bytes is refused rather than wrapped
+    assert lib.dca_prefill_workspace_bytes(65535, (1 << 30) - 1, 65535, 128, 128, 1) == 0
 
 
 def test_decode_workspace_sizes(lib):
@@ -136,6 +150,7 @@ def test_decode_rejects_before_touching_device(lib, over, status):
     ((FAKE, FAKE, 1, 8, 2, 64, 0, 0, 128, 128, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
     ((FAKE, FAKE + 2, 1, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),
     ((FAKE, FAKE, 0, 8, 2, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_OK),   # empty: no-op
+    ((FAKE, FAKE, 1, 8, 1 << 25, 64, 0, 0, 128, 32, 1e4, 1, None), _lib.DCA_ERR_INVALID_ARG),  # H * D = 2^31
 ])
 def test_remap_validation(lib, args, status):
     assert lib.dca_rope_remap(*args) == status
