@@ -213,7 +213,7 @@ __device__ inline int vt_perm(int p) { return (p & ~15) | (p & 3) | ((p & 4) << 
 
 // fp32 prepare pass (keys only; the fp32 kernels read V as it is): one
 // workgroup per (64-key tile, KV head, sequence), one rotary pair per thread.
-template <typename T, int D>
+template <int D>
 __global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
   constexpr int half = D / 2;
   constexpr int TK = kPrefillTileKeys;
@@ -221,42 +221,38 @@ __global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
   const int j0 = tile * TK;
   const int Lb = a.per_seq ? a.seq_len[b] : a.L;   // valid rows of this sequence
   const int64_t bg = (int64_t)b * a.Hkv + g;
-  const T* k = (const T*)a.k;
-  T* krot = (T*)a.krot;
-  T* k_rot_out = (T*)a.k_rot_out;
+  const float* k = (const float*)a.k;
+  float* krot = (float*)a.krot;
+  float* k_rot_out = (float*)a.k_rot_out;
   for (int idx = threadIdx.x; idx < TK * half; idx += 256) {
     const int row = idx / half, kk = idx - row * half;
     const int j = j0 + row;
-    T* dst = krot + (bg * a.Lp + j) * D;
+    float* dst = krot + (bg * a.Lp + j) * D + kk;
     const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : 0;
+    float y1 = 0.f, y2 = 0.f;   // rows past the sequence: zero
     if (j < Lb && crow < 0) {   // unreadable page: poison the key so the rows using it give NaN
-      Elem<T>::store(dst + kk, __builtin_nanf(""));
-      Elem<T>::store(dst + kk + half, __builtin_nanf(""));
+      y1 = y2 = __builtin_nanf("");
     } else if (j < Lb) {
-      const int64_t in = (crow * a.Hkv + g) * D;
-      const double x1 = Elem<T>::load(k + in + kk);
-      const double x2 = Elem<T>::load(k + in + kk + half);
+      const int64_t in = (crow * a.Hkv + g) * D + kk;
+      const double x1 = k[in], x2 = k[in + half];
       if (a.table || a.pos_mode == 1) {
         const double2 c = a.pos_mode == 1
                               ? rope_cs((double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk),
                                         a.theta[kk])
                               : a.table[((j / a.kdiv) % a.kmod) * half + kk];
-        const float y1 = (float)fma(x1, c.x, -(x2 * c.y));   // as rotate_pairs<float>
-        const float y2 = (float)fma(x2, c.x, x1 * c.y);
-        Elem<T>::store(dst + kk, y1);
-        Elem<T>::store(dst + kk + half, y2);
+        y1 = (float)fma(x1, c.x, -(x2 * c.y));   // as rotate_pairs<float>
+        y2 = (float)fma(x2, c.x, x1 * c.y);
         if (k_rot_out) {
-          Elem<T>::store(k_rot_out + in + kk, y1);
-          Elem<T>::store(k_rot_out + in + kk + half, y2);
+          k_rot_out[in] = y1;
+          k_rot_out[in + half] = y2;
         }
       } else {   // already rotated: exact copy
-        Elem<T>::store(dst + kk, (float)x1);
-        Elem<T>::store(dst + kk + half, (float)x2);
+        y1 = (float)x1;
+        y2 = (float)x2;
       }
-    } else {
-      Elem<T>::store(dst + kk, 0.f);
-      Elem<T>::store(dst + kk + half, 0.f);
     }
+    dst[0] = y1;
+    dst[half] = y2;
   }
 }
 
@@ -399,9 +395,9 @@ hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st) {
   if (dtype == 0) {
     const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)a.Hkv, (unsigned)a.B);
     if (a.D == 64)
-      hipLaunchKernelGGL((kv_prep_f32_kernel<float, 64>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_prep_f32_kernel<64>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((kv_prep_f32_kernel<float, 128>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_prep_f32_kernel<128>), grid, dim3(256), 0, st, a);
   } else {
     const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)((a.Hkv + kPrepHeads - 1) / kPrepHeads),
                     (unsigned)a.B);
