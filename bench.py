@@ -26,7 +26,9 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +74,74 @@ def measured_traffic(key):
         return t["bytes_per_launch"]
     except (OSError, ValueError, KeyError, TypeError):
         return None
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (the starred line of the
+    device's sysfs pp_dpm_sclk) from a background thread while a region runs.
+    Reports nothing when the file cannot be read."""
+
+    def __init__(self, dev, period_s=0.002):
+        self.path, self.power_path, self.samples, self.power, self.period = None, None, [], [], period_s
+        self._stop, self._thread = threading.Event(), None
+        try:
+            p = __import__("torch").cuda.get_device_properties(dev)
+            base = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+            if os.access(base + "/pp_dpm_sclk", os.R_OK):
+                self.path = base + "/pp_dpm_sclk"
+            for hw in sorted(os.listdir(base + "/hwmon")):
+                f = os.path.join(base, "hwmon", hw, "power1_input")
+                if os.access(f, os.R_OK):
+                    self.power_path = f
+                    break
+        except Exception:   # no device properties or no sysfs: report no clock
+            pass
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*mhz", line, re.I)
+                    return int(m.group(1)) if m else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except (OSError, ValueError):
+                return
+            if v:
+                self.samples.append(v)
+            if self.power_path:
+                try:
+                    with open(self.power_path) as f:
+                        self.power.append(int(f.read().strip()) / 1e6)   # microwatts
+                except (OSError, ValueError):
+                    self.power_path = None
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def summary(self):
+        """Statistics over the second half of the samples (the readings are
+        averages that trail a change of load)."""
+        if not self.samples:
+            return None
+        v = sorted(self.samples[len(self.samples) // 2:])
+        pw = sorted(self.power[len(self.power) // 2:])
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "power_w_median": pw[len(pw) // 2] if pw else None,
+                "source": "sysfs pp_dpm_sclk and hwmon power1_input, sampled during extra untimed attention calls"}
 
 
 def prefill_kernel_name(c, w, D):
@@ -247,6 +317,16 @@ def main():
                               "traffic": measured_traffic("prefill_attend"),
                               "kernel": prefill_kernel_name(P["c"], P["w"], P["D"]),
                               "kernel_ms": att_ms, "flops_per_launch": fl}
+        # the shader clock under this load, sampled over extra (untimed) attention
+        # calls: the spec peak assumes 2.4 GHz
+        with ClockSampler(dev) as clk:
+            for _ in range(max(5, int(600.0 / att_ms))):   # about 0.6 s of back-to-back calls
+                dca.prefill_attend(q, ws, P["Hkv"], P["c"], P["w"], out=o)
+            torch.cuda.synchronize()
+        clock = clk.summary()
+        result["roofline"]["clock"] = clock
+        if clock:
+            result["roofline"]["frac_at_clock"] = achieved / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0)
         att_all = sorted(e[1].elapsed_time(e[2]) for e in pe)
         # the prepare pass reads K and V once and writes the rotated keys and
         # the V tiles once (HBM-bound)
