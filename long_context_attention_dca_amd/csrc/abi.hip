@@ -89,15 +89,14 @@ struct DecodeLayout {
 };
 
 // kv: per-sequence cached key counts (host), or null for B sequences of
-// kv_len keys; kv_len is the longest sequence either way.  seg: per-sequence
-// key-segment boundaries (two key caches), or null.
-bool decode_layout(int64_t B, const int64_t* kv, const int64_t* seg, int64_t kv_len, int64_t Hq, int64_t Hkv,
-                   int64_t D, int dtype, DecodeLayout* out) {
+// kv_len keys; kv_len is the longest sequence either way.
+bool decode_layout(int64_t B, const int64_t* kv, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D, int dtype,
+                   DecodeLayout* out) {
   if (B < 1 || kv_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !head_dim_ok(D) || !dtype_ok(dtype))
     return false;
   if (B >= kMaxDim || kv_len >= kMaxDim / 2 || Hq >= 65536 || B * Hq >= kMaxDim) return false;
   DecodeLayout p;
-  decode_plan(kv, seg, B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
+  decode_plan(kv, B, kv_len, Hq, Hkv, dtype, &p.kps, &p.ns);
   p.qv = 0;
   p.part_o = (size_t)round_up(B * Hq * 3 * D * elem_size(dtype), 256);
   p.part_lse = p.part_o + (size_t)round_up(B * Hq * (int64_t)p.ns * D * 4, 256);
@@ -448,7 +447,7 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
 size_t dca_decode_workspace_bytes(int64_t B, int64_t kv_len, int64_t Hq, int64_t Hkv, int64_t D,
                                   int dtype) {
   DecodeLayout p;
-  return decode_layout(B, nullptr, nullptr, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
+  return decode_layout(B, nullptr, kv_len, Hq, Hkv, D, dtype, &p) ? p.total : 0;
 }
 
 int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -463,7 +462,7 @@ int dca_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
       (lse && !aligned(lse, 4)))
     return DCA_ERR_INVALID_ARG;
   DecodeLayout p;
-  if (!decode_layout(B, nullptr, nullptr, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
+  if (!decode_layout(B, nullptr, kv_len, Hq, Hkv, D, dtype, &p)) return DCA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
@@ -611,7 +610,8 @@ int64_t map_seg(const DecodeMap& m, int64_t kv) {
   return 0;
 }
 
-// Workspace layout of a ragged decode under a map (segments for two caches).
+// Workspace layout of a ragged decode under a map, and each sequence's first
+// key read from the main cache (two-cache maps).
 bool map_decode_layout(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int dtype,
                        const DecodeMap& m, DecodeLayout* p, std::vector<int64_t>* seg_out) {
   if (!kv_len || B < 1 || B >= kMaxDim) return false;
@@ -622,7 +622,7 @@ bool map_decode_layout(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv
     max_kv = kv_len[b] > max_kv ? kv_len[b] : max_kv;
     if (m.map != kMapDCA) seg[b] = map_seg(m, kv_len[b]);
   }
-  if (!decode_layout(B, kv_len, seg.empty() ? nullptr : seg.data(), max_kv, Hq, Hkv, D, dtype, p)) return false;
+  if (!decode_layout(B, kv_len, max_kv, Hq, Hkv, D, dtype, p)) return false;
   if (seg_out) *seg_out = seg;
   return true;
 }

@@ -137,10 +137,10 @@ struct DecodeArgs {
   PagedKv pg;          // kc / vc are page pools (cache_len unused), or bt null
   // Position map (PosMap).  SelfExtend and coarse / fine keep two key caches:
   // keys j < seg[b] (grouped, resp. two or more chunks before the query's)
-  // are read from kc2, the others from kc; each segment is cut into ranges
-  // of keys_per_split keys on its own.  DCA: seg[b] = 0, kc2 unused.  The
-  // query variants: DCA intra / succ / inter; SelfExtend grouped /
-  // neighbor; coarse / fine intra / succ / inter at real positions.
+  // are read from kc2, the others from kc; a key range may hold keys of
+  // both.  DCA: seg[b] = 0, kc2 unused.  The query variants: DCA intra /
+  // succ / inter; SelfExtend grouped / neighbor; coarse / fine intra / succ
+  // / inter at real positions.
   int map;
   const void* kc2;
   int seg[kMaxSeqGroup];
@@ -151,10 +151,8 @@ struct DecodeArgs {
 // Split plan shared by the workspace queries and the launchers: kv holds the
 // B sequences' cached key counts (host memory), or is null for B sequences
 // of uniform_kv keys.
-// seg: per-sequence segment boundaries (host memory, keys below are ranged
-// on their own), or null for one segment.
-void decode_plan(const int64_t* kv, const int64_t* seg, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv,
-                 int dtype, int* keys_per_split, int* nsplit);
+void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv, int dtype,
+                 int* keys_per_split, int* nsplit);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
 
 }  // namespace dca

@@ -48,24 +48,15 @@ __device__ inline int swz(int row, int chunk) {
 // The new token of sequence b sits at (its cached key count) - 1.
 __device__ inline int seq_keys(const DecodeArgs& a, int b) { return a.per_seq ? a.seq_len[b] : a.kv_len; }
 __host__ __device__ inline int seq_seg(const DecodeArgs& a, int b) { return a.per_seq ? a.seg[b] : 0; }
-// Key ranges of sequence b: ceil(seg / kps) over [0, seg), then
-// ceil((keys - seg) / kps) over [seg, keys).
-__host__ __device__ inline int seq_ranges(int keys, int seg, int kps) {
-  return (seg + kps - 1) / kps + (keys - seg + kps - 1) / kps;
-}
-// Key range `split` of sequence b: [kbeg, kend); second = read from kc2.
-__device__ inline void range_of(const DecodeArgs& a, int b, int split, int* kbeg, int* kend, bool* second) {
-  const int keys = seq_keys(a, b), seg = seq_seg(a, b), kps = a.keys_per_split;
-  const int n0 = (seg + kps - 1) / kps;
-  if (split < n0) {
-    *kbeg = split * kps;
-    *kend = min(*kbeg + kps, seg);
-    *second = true;
-  } else {
-    *kbeg = seg + (split - n0) * kps;
-    *kend = min(*kbeg + kps, keys);   // may be empty (ragged batch)
-    *second = false;
-  }
+// Key ranges of sequence b: ceil(keys / kps) ranges of kps keys.  Under the
+// two-cache maps a range may hold keys of both caches: keys below seg[b]
+// are read from kc2, the others from kc.
+__host__ __device__ inline int seq_ranges(int keys, int kps) { return (keys + kps - 1) / kps; }
+// Key range `split` of sequence b: [kbeg, kend), empty past its last range.
+__device__ inline void range_of(const DecodeArgs& a, int b, int split, int* kbeg, int* kend) {
+  const int keys = seq_keys(a, b), kps = a.keys_per_split;
+  *kbeg = split * kps;
+  *kend = min(*kbeg + kps, keys);
 }
 
 template <typename T>
@@ -99,8 +90,9 @@ __global__ void decode_qprep_kernel(DecodeArgs a) {
 
 // ---- 2. split kernel, bf16 MFMA ----------------------------------------------------
 // PAGED: the caches are page pools (a.pg); the dense instantiation carries
-// none of the block-table work.
-template <int D, bool PAGED>
+// none of the block-table work.  TWO: a map with two key caches (SelfExtend,
+// coarse / fine); the DCA instantiation carries none of that work.
+template <int D, bool PAGED, bool TWO>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   constexpr int NDS = D / 16;
@@ -146,17 +138,22 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   const int hq = g * G + (qvalid ? qi : 0);
   const int kv_len = seq_keys(a, b), s = a.s;
   int kbeg, kend;
-  bool second;
-  range_of(a, b, split, &kbeg, &kend, &second);
+  range_of(a, b, split, &kbeg, &kend);
   const int qpos = kv_len - 1;
   const int nq = qpos / s;
-  // SelfExtend: one relation per segment (grouped below seg, neighbor above)
-  const int seg_cls = second ? 0 : 1;
+  // Two caches: keys below seg come from kc2 (SelfExtend: grouped keys,
+  // relation 0; coarse / fine: coarse-scaled keys, relation 2), the others
+  // from kc (SelfExtend: neighbor keys, relation 1; coarse / fine: plain keys,
+  // relation 0 or 1 by chunk).
+  const int seg = TWO ? seq_seg(a, b) : 0;
 
   uint8_t* kl = smem + wave * WBYTES;
   uint8_t* vl = kl + KBYTES;
   const int64_t row_stride = (int64_t)a.Hkv * D;  // elements between consecutive cache rows
-  const uint16_t* kc = (const uint16_t*)(second ? a.kc2 : a.kc) + (int64_t)g * D;
+  const uint16_t* kc = (const uint16_t*)a.kc + (int64_t)g * D;
+  const uint16_t* kc2 = TWO ? (const uint16_t*)a.kc2 + (int64_t)g * D : kc;
+  // cache holding the key rows of the sub-tile starting at j0 (its first key's)
+  auto kbase = [&](int j0) { return (TWO && j0 < seg) ? kc2 : kc; };
   const uint16_t* vc = (const uint16_t*)a.vc + (int64_t)g * D;
   const uint16_t* qv = (const uint16_t*)a.qv + ((int64_t)b * a.Hq + hq) * 3 * D;
 
@@ -204,13 +201,13 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
     return (const uint4*)(sb + lo);
   };
   uint4 kreg[NI], vreg[NI];
-  auto gload_k = [&](int j0) {
+  auto gload_k = [&](int j0, const uint16_t* kb) {
     uint32_t lo = lane_off;
     asm volatile("" : "+v"(lo));
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int j = j0 + (it * 64 + lane) / CPR;
-      kreg[it] = (j < kend) ? *paddr(kc, it, lo) : make_uint4(0, 0, 0, 0);
+      kreg[it] = (j < kend) ? *paddr(kb, it, lo) : make_uint4(0, 0, 0, 0);
     }
   };
   auto gload_v = [&](int j0) {
@@ -261,7 +258,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
   int cur_cls = -1;
 
   rows_of(kbeg);
-  gload_k(kbeg);
+  gload_k(kbeg, kbase(kbeg));
   gload_v(kbeg);
   for (int j0 = kbeg; j0 < kend; j0 += SUB) {
     __builtin_amdgcn_wave_barrier();
@@ -271,17 +268,43 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
     lstore_k();
     if (more) {
       rows_of(j0 + SUB);
-      gload_k(j0 + SUB);
+      gload_k(j0 + SUB, kbase(j0 + SUB));
     }
     lstore_v();
     if (more) gload_v(j0 + SUB);
     __builtin_amdgcn_wave_barrier();
 
     const int jl = min(j0 + SUB, kend) - 1;
-    const bool se = a.map == kMapSelfExtend;
-    const int cls_lo = se ? seg_cls : min(nq - jl / s, 2), cls_hi = se ? seg_cls : min(nq - j0 / s, 2);
-    const bool straddle = cls_lo != cls_hi;
     const bool tail = j0 + SUB > kend;
+    // Two caches: a sub-tile holding keys of both is processed twice, first
+    // its kc2 keys (staged above), then its kc keys, re-staged from kc.
+    const bool two_pass = TWO && j0 < seg && seg <= jl;
+    for (int pass = 0; pass < (two_pass ? 2 : 1); ++pass) {
+    int plo = j0, phi = jl;   // keys of this pass
+    if constexpr (TWO) {
+      if (two_pass) {
+        if (pass == 0) {
+          phi = seg - 1;
+        } else {
+          plo = seg;
+          // K rows of this sub-tile from kc, then the next sub-tile's load
+          // again (its registers were taken)
+          __builtin_amdgcn_wave_barrier();
+          rows_of(j0);
+          gload_k(j0, kc);
+          lstore_k();
+          if (more) {
+            rows_of(j0 + SUB);
+            gload_k(j0 + SUB, kbase(j0 + SUB));
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+    }
+    const bool se = a.map == kMapSelfExtend;
+    const int se_cls = (TWO && plo < seg) ? 0 : 1;
+    const int cls_lo = se ? se_cls : min(nq - phi / s, 2), cls_hi = se ? se_cls : min(nq - plo / s, 2);
+    const bool straddle = cls_lo != cls_hi;
     // A sub-tile spanning several relations is processed once per relation
     // with the other pairs masked; the online softmax merges the pieces.
     for (int cls = cls_lo; cls <= cls_hi; ++cls) {
@@ -304,11 +327,11 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
         const bf16x8 kf = *(const bf16x8*)(kl + ql * (D * 2) + swz<CPR>(ql, ch) * 16);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc, 0, 0, 0);
       }
-      if (tail || straddle) {
-        // Keys kept: the split's range, intersected on a straddling sub-tile
-        // with the key range of relation `cls` (intra: chunk nq, successive:
-        // chunk nq-1, inter: chunks < nq-1).
-        int lo = kbeg, hi = kend - 1;
+      if (tail || straddle || two_pass) {
+        // Keys kept: the split's range and the pass's keys, intersected on a
+        // straddling sub-tile with the key range of relation `cls` (intra:
+        // chunk nq, successive: chunk nq-1, inter: chunks < nq-1).
+        int lo = max(kbeg, plo), hi = min(kend - 1, phi);
         if (straddle) {
           lo = max(lo, cls == 0 ? nq * s : (cls == 1 ? (nq - 1) * s : 0));
           hi = min(hi, cls == 0 ? qpos : (cls == 1 ? nq * s - 1 : (nq - 1) * s - 1));
@@ -355,6 +378,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
       }
       l_run += lsum;
     }
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -387,14 +411,15 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
   const int G = a.Hq / a.Hkv, g = hq / G;
   const int kv_len = seq_keys(a, b), s = a.s;
   int kbeg, kend;
-  bool second;
-  range_of(a, b, split, &kbeg, &kend, &second);   // past the sequence's ranges: empty
+  range_of(a, b, split, &kbeg, &kend);   // past the sequence's ranges: empty
+  const int seg = a.map == kMapDCA ? 0 : seq_seg(a, b);   // keys below seg: from kc2
   const int nq = (kv_len - 1) / s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float* qv = (const float*)a.qv + (int64_t)bh * 3 * D;
   for (int idx = tid; idx < 3 * D; idx += 256) qs[idx / D][idx % D] = qv[idx];
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const float* kc = (const float*)(second ? a.kc2 : a.kc) + (int64_t)g * D;
+  const float* kc = (const float*)a.kc + (int64_t)g * D;
+  const float* kc2 = a.map == kMapDCA ? kc : (const float*)a.kc2 + (int64_t)g * D;
   const float* vc = (const float*)a.vc + (int64_t)g * D;
   __shared__ int64_t rows[256];   // cache row of each key of the current step (-1: unreadable page)
   float m = -INFINITY, l = 0.f, o = 0.f;  // thread tid < D owns output dim tid
@@ -408,8 +433,8 @@ __global__ void __launch_bounds__(256) decode_split_f32_kernel(DecodeArgs a) {
       if (row < 0) {
         x = __builtin_nanf("");   // unreadable page: the row's result becomes NaN
       } else {
-        const int cls = a.map == kMapSelfExtend ? (second ? 0 : 1) : min(nq - j / s, 2);
-        const float* kr = kc + row * row_stride;
+        const int cls = a.map == kMapSelfExtend ? (j < seg ? 0 : 1) : min(nq - j / s, 2);
+        const float* kr = (j < seg ? kc2 : kc) + row * row_stride;
         float acc = 0.f;
         for (int d = 0; d < D; ++d) acc = fmaf(qs[cls][d], kr[d], acc);
         x = acc * a.sm_scale;
@@ -461,7 +486,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
   float* __restrict__ lse = a.lse;
   const int D = a.D;
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const int ns = seq_ranges(seq_keys(a, bh / a.Hq), seq_seg(a, bh / a.Hq), a.keys_per_split);
+  const int ns = seq_ranges(seq_keys(a, bh / a.Hq), a.keys_per_split);
   const float* pl = a.part_lse + (int64_t)bh * a.nsplit;
   float M = -INFINITY;
   for (int i = tid; i < ns; i += 128) M = fmaxf(M, pl[i]);
@@ -491,8 +516,8 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-void decode_plan(const int64_t* kv, const int64_t* seg, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv,
-                 int dtype, int* keys_per_split, int* nsplit) {
+void decode_plan(const int64_t* kv, int64_t B, int64_t uniform_kv, int64_t Hq, int64_t Hkv, int dtype,
+                 int* keys_per_split, int* nsplit) {
   // One wave per key range, as many ranges as the chip holds at once: MI355X
   // runs 8 of these waves per CU (2 per SIMD) on 256 CUs.  The range length is
   // the shortest multiple of 32 keys whose ranges, over the whole batch (a
@@ -503,10 +528,7 @@ void decode_plan(const int64_t* kv, const int64_t* seg, int64_t B, int64_t unifo
   const int64_t waves_per_key = dtype == 0 ? Hq : Hkv * ((G + 31) / 32);  // waves reading one cached key
   const int64_t target = 2048;
   auto len = [&](int64_t b) { return kv ? kv[b] : uniform_kv; };
-  auto ranges = [&](int64_t b, int64_t kps) {
-    const int64_t n = len(b), sg = seg ? seg[b] : 0;
-    return (sg + kps - 1) / kps + (n - sg + kps - 1) / kps;
-  };
+  auto ranges = [&](int64_t b, int64_t kps) { return (len(b) + kps - 1) / kps; };
   int64_t max_kv = 0;
   for (int64_t b = 0; b < B; ++b) max_kv = len(b) > max_kv ? len(b) : max_kv;
   auto waves = [&](int64_t kps) {
@@ -517,10 +539,9 @@ void decode_plan(const int64_t* kv, const int64_t* seg, int64_t B, int64_t unifo
   };
   // Search in units of SUB keys.  At least 256 keys per range, and at most
   // kMaxSplits ranges per sequence (the combine kernel keeps one weight per
-  // range in LDS; a second segment can add one range).  waves() never grows
-  // with the range length; if even one range per segment overflows the
-  // round, the whole length is taken.
-  const int64_t cap = seg ? kMaxSplits - 1 : kMaxSplits;
+  // range in LDS).  waves() never grows with the range length; if even one
+  // range per sequence overflows the round, the whole length is taken.
+  const int64_t cap = kMaxSplits;
   int64_t lo = (max_kv + cap - 1) / cap;
   lo = (round_up(lo < 256 ? 256 : lo, SUB)) / SUB;
   int64_t hi = round_up(max_kv, SUB) / SUB;
@@ -554,22 +575,26 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
     if (a.per_seq) {   // flat numbering of the real ranges, sequence by sequence
       b.wave_start[0] = 0;
       for (int i = 0; i < a.B; ++i)
-        b.wave_start[i + 1] = b.wave_start[i] + seq_ranges(a.seq_len[i], a.seg[i], a.keys_per_split) * a.Hkv * nqg;
+        b.wave_start[i + 1] = b.wave_start[i] + seq_ranges(a.seq_len[i], a.keys_per_split) * a.Hkv * nqg;
       waves = b.wave_start[a.B];
     }
     const dim3 grid((unsigned)((waves + 3) / 4));
     const float scale_log2 = a.sm_scale * kLog2e;
-    const bool paged = a.pg.bt != nullptr;
+    const bool paged = a.pg.bt != nullptr, two = a.map != kMapDCA;   // two-cache maps are never paged
     if (a.D == 64) {
-      if (paged)
-        hipLaunchKernelGGL((decode_split_bf16_kernel<64, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      if (two)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, false, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      else if (paged)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, true, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
       else
-        hipLaunchKernelGGL((decode_split_bf16_kernel<64, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, false, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
     } else {
-      if (paged)
-        hipLaunchKernelGGL((decode_split_bf16_kernel<128, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      if (two)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, false, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      else if (paged)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, true, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
       else
-        hipLaunchKernelGGL((decode_split_bf16_kernel<128, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, false, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
     }
     hipLaunchKernelGGL(decode_combine_kernel<uint16_t>, dim3(nbh), dim3(128), 0, st, a);
   }
