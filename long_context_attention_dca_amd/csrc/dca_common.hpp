@@ -152,6 +152,26 @@ __device__ inline uint4 pack_bf16x8(const float* f) {
   return u;
 }
 
+// 16-byte global load with the non-temporal hint (the `nt` bit): for data
+// streamed through once, which is then not kept in L2 / MALL.  A plain read
+// of a 6.55 GB buffer measured 6.1 TB/s, the same read with the hint
+// 6.7-6.8 TB/s.
+__device__ inline uint4 load_stream(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+// 16-byte global store with the non-temporal hint, for output that is not
+// read again soon.
+__device__ inline void store_stream(uint4* p, const uint4& v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 t;
+  t[0] = v.x;
+  t[1] = v.y;
+  t[2] = v.z;
+  t[3] = v.w;
+  __builtin_nontemporal_store(t, (u32x4*)p);
+}
 template <typename T>
 struct Elem;
 template <>

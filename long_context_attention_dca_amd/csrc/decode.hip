@@ -207,7 +207,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int j = j0 + (it * 64 + lane) / CPR;
-      kreg[it] = (j < kend) ? *paddr(kb, it, lo) : make_uint4(0, 0, 0, 0);
+      kreg[it] = (j < kend) ? load_stream(paddr(kb, it, lo)) : make_uint4(0, 0, 0, 0);
     }
   };
   auto gload_v = [&](int j0) {
@@ -216,7 +216,7 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int j = j0 + (it * 64 + lane) / CPR;
-      vreg[it] = (j < kend) ? *paddr(vc, it, lo) : make_uint4(0, 0, 0, 0);
+      vreg[it] = (j < kend) ? load_stream(paddr(vc, it, lo)) : make_uint4(0, 0, 0, 0);
     }
   };
   auto lstore_k = [&]() {

@@ -167,11 +167,11 @@ __global__ void __launch_bounds__(256) rope_remap_kernel(const T* __restrict__ x
     const int g = r % NG, th = r / NG, h = th % H, tk = th / H;
     const int64_t off = ((b * L + t0 + tk) * H + h) * D + g * N;
     float x1[N], x2[N];
-    Vec16<T>::unpack(*(const uint4*)(x + off), x1);
-    Vec16<T>::unpack(*(const uint4*)(x + off + half), x2);
+    Vec16<T>::unpack(load_stream((const uint4*)(x + off)), x1);
+    Vec16<T>::unpack(load_stream((const uint4*)(x + off + half)), x2);
     rotate_pairs<T, N>(x1, x2, &cs[tk][g * N]);
-    *(uint4*)(out + off) = Vec16<T>::pack(x1);
-    *(uint4*)(out + off + half) = Vec16<T>::pack(x2);
+    store_stream((uint4*)(out + off), Vec16<T>::pack(x1));
+    store_stream((uint4*)(out + off + half), Vec16<T>::pack(x2));
     b += step_b;
     r += step_r;
     if (r >= inner) {
@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
       const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : -1;
 #pragma unroll
       for (int hh = 0; hh < kPrepHeads; ++hh)
-        vr[hh][it] = (hh < nh && crow >= 0) ? *(const uint4*)(vv + (crow * a.Hkv + h0 + hh) * D + dg * 8)
+        vr[hh][it] = (hh < nh && crow >= 0) ? load_stream((const uint4*)(vv + (crow * a.Hkv + h0 + hh) * D + dg * 8))
                                             : make_uint4(0, 0, 0, 0);
     }
   }
@@ -313,8 +313,8 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
     for (int hh = 0; hh < kPrepHeads; ++hh)
       if (hh < nh && valid) {
         const uint16_t* src = k + (crow * a.Hkv + h0 + hh) * D + k0;
-        x1[hh] = *(const uint4*)src;
-        x2[hh] = *(const uint4*)(src + half);
+        x1[hh] = load_stream((const uint4*)src);
+        x2[hh] = load_stream((const uint4*)(src + half));
       }
     double2 cs[8];
     if (valid && rotate) {
