@@ -401,9 +401,10 @@ def main():
         dvws = torch.empty(dca.decode_varlen_workspace_bytes(kvr, DC["Hq"], DC["Hkv"], DC["D"], torch.bfloat16),
                            dtype=torch.uint8, device=dev)
         # Warm-up: right after caches are built or copied, the first ~10 decode
-        # calls run up to 7 % slower than the steady state (measured); each
-        # line below is timed after MAP_WARMUP untimed calls.
-        MAP_WARMUP = 20
+        # calls (about 10 ms) run up to 7 % slower than the steady state
+        # (measured); each line below is timed after MAP_WARMUP untimed calls
+        # (about 40 ms).
+        MAP_WARMUP = 50
         for _ in range(MAP_WARMUP):
             dca.decode_varlen(dq, kc, vc, kvr, DC["c"], DC["w"], DC["base"], workspace=dvws)
         torch.cuda.synchronize()
