@@ -402,6 +402,34 @@ int dca_coarse_fine_key_remap(const void* x, void* out, int64_t B, int64_t L, in
                               int64_t pos0, int chunk, int train_len, int target_len, double rope_base,
                               int dtype, void* stream);
 
+/*
+ * dca_selfextend_decode_paged, dca_coarse_fine_decode_paged: the two map
+ * decodes above over page pools, with the same results (paging moves rows
+ * only; see dca_decode_paged for the block-table layout and its rules).
+ *
+ *   k_pages, k_pages_2nd, v_pages : pools [num_pages, page_size, Hkv, D]; the
+ *              two key pools hold the two rotations of the same rows
+ *              (k_pages at j; k_pages_2nd grouped, resp. coarse-scaled), so
+ *              one block table addresses all three pools.
+ *   block_table : DEVICE int32 [B, max_blocks]; page_size a multiple of 16;
+ *              kv_len[b] <= max_blocks * page_size.
+ *   ws       : dca_selfextend_decode_workspace_bytes, resp.
+ *              dca_coarse_fine_decode_workspace_bytes (as for the dense caches).
+ * An entry outside [0, num_pages) is never dereferenced; results of that
+ * sequence that would use it become NaN.  Everything else as in the dense
+ * map decodes.
+ */
+int dca_selfextend_decode_paged(const void* q, const void* k_pages, const void* k_pages_2nd, const void* v_pages,
+                                const int32_t* block_table, void* o, float* lse, const int64_t* kv_len, int64_t B,
+                                int64_t num_pages, int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv,
+                                int64_t D, int group, int window, double rope_base, float sm_scale, int dtype,
+                                void* ws, size_t ws_bytes, void* stream);
+int dca_coarse_fine_decode_paged(const void* q, const void* k_pages, const void* k_pages_2nd, const void* v_pages,
+                                 const int32_t* block_table, void* o, float* lse, const int64_t* kv_len, int64_t B,
+                                 int64_t num_pages, int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv,
+                                 int64_t D, int chunk, int train_len, int target_len, double rope_base,
+                                 float sm_scale, int dtype, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -445,6 +445,52 @@ def coarse_fine_decode(q, k_cache, k_cache_scaled, v_cache, kv_len, chunk: int, 
                        sm_scale, return_lse, workspace, "k_cache_scaled")
 
 
+def _map_decode_paged(fn_ws, fn, q, k_pages, k2_pages, v_pages, block_table, kv_len, params, base, sm_scale,
+                      return_lse, workspace, name):
+    lib = _lib.load()
+    _check(q, "q", 3)
+    num_pages, page_size, Hkv, max_blocks = _check_pages(k_pages, v_pages, block_table, q)
+    _check(k2_pages, name, 4, q.dtype)
+    if k2_pages.shape != k_pages.shape:
+        raise ValueError(f"{name} and k_pages differ in shape")
+    B, Hq, D = q.shape
+    if k_pages.shape[3] != D or block_table.shape[0] != B:
+        raise ValueError("page pool / block table shapes do not match q")
+    code = _dtype_code(q)
+    kl, _ = _host_i64(kv_len, B, "kv_len")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = int(getattr(lib, fn_ws)(kl, B, Hq, Hkv, D, *params[0], code))
+    if nbytes == 0:
+        raise ValueError("invalid decode sizes")
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check(fn, getattr(lib, fn)(
+        q.data_ptr(), k_pages.data_ptr(), k2_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+        o.data_ptr(), _ptr(lse), kl, B, num_pages, page_size, max_blocks, Hq, Hkv, D, *params[1], float(base),
+        float(sm_scale or 0.0), code, ws.data_ptr(), nbytes, _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def selfextend_decode_paged(q, k_pages, k_pages_grouped, v_pages, block_table, kv_len, group: int, window: int,
+                            base: float = 10000.0, sm_scale: float | None = None, return_lse: bool = False,
+                            workspace=None):
+    """selfextend_decode over page pools [num_pages, page_size, Hkv, D] (keys at j, keys
+    at floor(j / group), values) sharing one int32 block table [B, max_blocks]."""
+    return _map_decode_paged("dca_selfextend_decode_workspace_bytes", "dca_selfextend_decode_paged", q, k_pages,
+                             k_pages_grouped, v_pages, block_table, kv_len, ((group, window), (group, window)),
+                             base, sm_scale, return_lse, workspace, "k_pages_grouped")
+
+
+def coarse_fine_decode_paged(q, k_pages, k_pages_scaled, v_pages, block_table, kv_len, chunk: int, train_len: int,
+                             target_len: int, base: float = 10000.0, sm_scale: float | None = None,
+                             return_lse: bool = False, workspace=None):
+    """coarse_fine_decode over page pools (keys at j, coarse-scaled keys, values) sharing
+    one int32 block table [B, max_blocks]."""
+    return _map_decode_paged("dca_coarse_fine_decode_workspace_bytes", "dca_coarse_fine_decode_paged", q, k_pages,
+                             k_pages_scaled, v_pages, block_table, kv_len, ((chunk,), (chunk, train_len, target_len)),
+                             base, sm_scale, return_lse, workspace, "k_pages_scaled")
+
+
 def coarse_fine_key_remap(x, chunk: int, train_len: int, target_len: int, base: float = 10000.0, pos0: int = 0,
                           out=None):
     """Rotate x [B, L, H, D] (positions pos0 ..) at the coarse-scaled key positions."""

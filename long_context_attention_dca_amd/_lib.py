@@ -66,6 +66,10 @@ SIGNATURES = {
                                       _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_coarse_fine_key_remap": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _dbl, _int,
                                          _vp]),
+    "dca_selfextend_decode_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64,
+                                           _i64, _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_coarse_fine_decode_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64,
+                                            _i64, _i64, _int, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
 }
 
 _lib = None

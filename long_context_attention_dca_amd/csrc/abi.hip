@@ -681,7 +681,7 @@ int decode_varlen_impl(const void* q, const void* k_cache, const void* v_cache, 
     for (int i = 0; i < nb; ++i) a.seq_len[i] = (int)kv_len[b0 + i];
     a.map = dm.map;
     if (dm.map != kMapDCA) {
-      a.kc2 = (const uint8_t*)dm.kc2 + b0 * cache_len * Hkv * D * es;
+      a.kc2 = (const uint8_t*)dm.kc2 + (pg.bt ? 0 : b0 * cache_len * Hkv * D * es);
       for (int i = 0; i < nb; ++i) a.seg[i] = (int)seg[b0 + i];
     }
     a.se_group = dm.se_group;
@@ -811,6 +811,46 @@ int dca_coarse_fine_decode(const void* q, const void* k_cache, const void* k_cac
   // the chunk relation uses chunk size C (held in c and s)
   return decode_varlen_impl(q, k_cache, v_cache, o, lse, kv_len, B, cache_len, Hq, Hkv, D, chunk, 0, rope_base,
                             sm_scale, dtype, ws, ws_bytes, stream, PagedKv{}, m);
+}
+
+// The two-cache map decodes over page pools: both key pools and the value
+// pool share one block table.
+int dca_selfextend_decode_paged(const void* q, const void* k_pages, const void* k_pages_2nd, const void* v_pages,
+                                const int32_t* block_table, void* o, float* lse, const int64_t* kv_len, int64_t B,
+                                int64_t num_pages, int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv,
+                                int64_t D, int group, int window, double rope_base, float sm_scale, int dtype,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (!se_ok(group, window) || !k_pages_2nd) return DCA_ERR_INVALID_ARG;
+  PagedKv pg;
+  if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
+  DecodeMap m;
+  m.map = kMapSelfExtend;
+  m.kc2 = k_pages_2nd;
+  m.se_group = group;
+  m.se_window = window;
+  const int unbounded = 1 << 30;   // no chunk relation: s never splits a range
+  return decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, max_blocks * page_size, Hq, Hkv, D, unbounded,
+                            0, rope_base, sm_scale, dtype, ws, ws_bytes, stream, pg, m);
+}
+
+int dca_coarse_fine_decode_paged(const void* q, const void* k_pages, const void* k_pages_2nd, const void* v_pages,
+                                 const int32_t* block_table, void* o, float* lse, const int64_t* kv_len, int64_t B,
+                                 int64_t num_pages, int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv,
+                                 int64_t D, int chunk, int train_len, int target_len, double rope_base,
+                                 float sm_scale, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  if (chunk < 1 || chunk > (1 << 24) || train_len < 1 || target_len < 1 || !k_pages_2nd)
+    return DCA_ERR_INVALID_ARG;
+  PagedKv pg;
+  if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
+  DecodeMap m;
+  m.map = kMapCoarseFine;
+  m.kc2 = k_pages_2nd;
+  m.cf_chunk = chunk;
+  m.cf_inv_kappa = (double)train_len / (double)target_len;
+  return decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, max_blocks * page_size, Hq, Hkv, D, chunk, 0,
+                            rope_base, sm_scale, dtype, ws, ws_bytes, stream, pg, m);
 }
 
 int dca_coarse_fine_key_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, int64_t D, int64_t pos0,

@@ -580,16 +580,20 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st) {
     }
     const dim3 grid((unsigned)((waves + 3) / 4));
     const float scale_log2 = a.sm_scale * kLog2e;
-    const bool paged = a.pg.bt != nullptr, two = a.map != kMapDCA;   // two-cache maps are never paged
+    const bool paged = a.pg.bt != nullptr, two = a.map != kMapDCA;
     if (a.D == 64) {
-      if (two)
+      if (two && paged)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<64, true, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      else if (two)
         hipLaunchKernelGGL((decode_split_bf16_kernel<64, false, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
       else if (paged)
         hipLaunchKernelGGL((decode_split_bf16_kernel<64, true, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
       else
         hipLaunchKernelGGL((decode_split_bf16_kernel<64, false, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);
     } else {
-      if (two)
+      if (two && paged)
+        hipLaunchKernelGGL((decode_split_bf16_kernel<128, true, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
+      else if (two)
         hipLaunchKernelGGL((decode_split_bf16_kernel<128, false, true>), grid, dim3(256), 0, st, b, nqg, scale_log2);
       else if (paged)
         hipLaunchKernelGGL((decode_split_bf16_kernel<128, true, false>), grid, dim3(256), 0, st, b, nqg, scale_log2);

@@ -373,3 +373,27 @@ def test_map_decode_workspace_and_validation(lib):
     a = list(ok)
     a[3] = 0   # no rows: nothing to do
     assert lib.dca_coarse_fine_key_remap(*a) == 0
+
+
+@pytest.mark.parametrize("fn,params", [("dca_selfextend_decode_paged", (4, 100)),
+                                       ("dca_coarse_fine_decode_paged", (64, 1, 8))])
+def test_map_decode_paged_validation(lib, fn, params):
+    # q, k_pages, k_pages_2nd, v_pages, block_table, o, lse, kv_len, B, num_pages, page_size, max_blocks,
+    # Hq, Hkv, D, <map params>, base, sm_scale, dtype, ws, ws_bytes, stream
+    n = len(params)
+    ok = ([FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(40, 100), 2, 20, 16, 8, 8, 2, 64] + list(params)
+          + [1e4, 0.0, 1, FAKE_WS, 1 << 30, None])
+    f = getattr(lib, fn)
+    for i, bad, st in [(2, None, -1),            # no second key pool
+                       (4, None, -1),            # no block table
+                       (10, 24, -1),             # page size not a multiple of 16
+                       (7, _i64s(40, 129), -1),  # 129 rows > 8 blocks of 16
+                       (13, 3, -1),              # Hq % Hkv
+                       (14, 96, -2), (17 + n, 3, -2),
+                       (19 + n, 64, -3), (18 + n, None, -3)]:
+        a = list(ok)
+        a[i] = bad
+        assert f(*a) == st, (fn, i, bad)
+    a = list(ok)
+    a[15] = 0            # SelfExtend group 0 / coarse-fine chunk 0
+    assert f(*a) == -1

@@ -144,3 +144,57 @@ def test_decode_paged_100k_workload():
         Od, _ = oracle.dca_decode_ref(qd[b: b + 1], k[b: b + 1, : kv[b]], v[b: b + 1, : kv[b]], c, w, P_["base"])
         mx, _ = assert_close(o[b], Od[0], torch.bfloat16, f"paged decode seq {b}")
         log(f"  paged decode seq {b} (kv_len {kv[b]}): max abs {mx:.3e}")
+
+
+MAP_PAGED = [
+    # name, map, kv list, Hq, Hkv, D, params, page, dtype
+    ("se_bf16_p16", "selfextend", [1, 50, 99, 100, 101, 700], 8, 2, 128, (4, 100), 16, torch.bfloat16),
+    ("se_bf16_p48_long", "selfextend", [4097, 2500, 9000], 64, 8, 128, (8, 1024), 48, torch.bfloat16),
+    ("se_f32_p32", "selfextend", [1, 34, 35, 600], 4, 2, 64, (5, 33), 32, torch.float32),
+    ("cf_bf16_p16", "coarse_fine", [1, 64, 65, 128, 129, 700], 8, 2, 128, (64, 1, 8), 16, torch.bfloat16),
+    ("cf_bf16_p64_guide", "coarse_fine", [600, 2048, 5000], 16, 2, 128, (512, 4096, 32768), 64, torch.bfloat16),
+    ("cf_f32_p16", "coarse_fine", [1, 13, 14, 27, 400], 4, 2, 64, (13, 2, 9), 16, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", MAP_PAGED, ids=[c[0] for c in MAP_PAGED])
+def test_map_decode_paged_matches_oracle_and_dense(case):
+    # Both rotated key pools and the value pool share one block table (the same
+    # page order for all three).  Oracle from the raw keys; the dense map decode
+    # on the same rows gives the same bits.
+    name, which, kv, Hq, Hkv, D, params, P, dtype = case
+    log(f"[map decode paged] {name}")
+    B, L = len(kv), max(kv)
+    qd, k, v = inputs.decode_inputs(B, L, Hq, Hkv, D, dtype, seed=503, qk_scale=2.0)
+    kg = k.to(dev())
+    k_plain = dca.rope_remap(kg, dca.DCA_MAP_PLAIN, 1, 0)
+    if which == "selfextend":
+        G, W = params
+        k_2nd = dca.rope_remap(kg, dca.DCA_MAP_SE_KEY_GROUPED, G, W)
+        dense = lambda: dca.selfextend_decode(qd.to(dev()), k_plain, k_2nd, v.to(dev()), kv, G, W, return_lse=True)
+        paged = lambda a, b_, c_, t: dca.selfextend_decode_paged(qd.to(dev()), a, b_, c_, t, kv, G, W,
+                                                                  return_lse=True)
+        O, _ = oracle.selfextend_decode_ref(qd, k, v, kv, G, W)
+    else:
+        C, tr, tg = params
+        k_2nd = dca.coarse_fine_key_remap(kg, C, tr, tg)
+        dense = lambda: dca.coarse_fine_decode(qd.to(dev()), k_plain, k_2nd, v.to(dev()), kv, C, tr, tg,
+                                               return_lse=True)
+        paged = lambda a, b_, c_, t: dca.coarse_fine_decode_paged(qd.to(dev()), a, b_, c_, t, kv, C, tr, tg,
+                                                                   return_lse=True)
+        O, _ = oracle.coarse_fine_decode_ref(qd, k, v, kv, C, tr, tg)
+    kp, table = to_pages(k_plain, kv, P, seed=7)
+    k2p, _ = to_pages(k_2nd, kv, P, seed=7)
+    vp, _ = to_pages(v.to(dev()), kv, P, seed=7)
+    o, lse = paged(kp, k2p, vp, table)
+    got = to_np(o)
+    for b in range(B):
+        assert_close(got[b], O[b], dtype, f"{name} seq {b}")
+    od, lsed = dense()
+    assert torch.equal(o, od) and torch.equal(lse, lsed)
+    # an entry outside the pool poisons only its own sequence
+    bad_table = table.clone()
+    bad_table[B - 1, 0] = kp.shape[0] + 3
+    ob, _ = paged(kp, k2p, vp, bad_table)
+    assert torch.isnan(ob[B - 1]).all()
+    assert torch.equal(ob[: B - 1], o[: B - 1])
