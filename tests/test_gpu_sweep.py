@@ -6,7 +6,8 @@ hundred (tile multiples and ragged tails alike), GQA ratios 1 / 2 / 4, both
 head dims, both dtypes, and the map parameters over their whole valid range
 (chunk sizes that straddle tiles, w = 0, windows wider than the sequence,
 group 1, chunk offsets that are and are not multiples of 32, page sizes
-16 / 32 / 48 / 64), and the SelfExtend and coarse / fine decodes.  Inputs are the discriminating ones (q, k scaled by 2).
+16 / 32 / 48 / 64), and the SelfExtend and coarse / fine decodes (dense, and
+from page pools, which must give the same bits).  Inputs are the discriminating ones (q, k scaled by 2).
 Bars: fp32 max-abs <= 1e-4; bf16 max-abs <= 2e-2 and mean-abs <= 2e-3.
 """
 import numpy as np
@@ -152,10 +153,18 @@ def test_sweep_selfextend_decode(idx):
     kg = k.to(dev())
     kp = _nan_tails(dca.rope_remap(kg, dca.DCA_MAP_PLAIN, 1, 0), kv)
     kq = _nan_tails(dca.rope_remap(kg, dca.DCA_MAP_SE_KEY_GROUPED, grp, win), kv)
-    o = to_np(dca.selfextend_decode(qd.to(dev()), kp, kq, _nan_tails(v.to(dev()), kv), kv, grp, win))
+    vd = _nan_tails(v.to(dev()), kv)
+    od = dca.selfextend_decode(qd.to(dev()), kp, kq, vd, kv, grp, win)
+    o = to_np(od)
     O, _ = oracle.selfextend_decode_ref(qd, k, v, kv, grp, win)
     for b in range(B):
         assert_close(o[b], O[b], dtype, f"selfextend decode seq {b}")
+    # the same rows from page pools: the same bits
+    P = int(rng.choice([16, 32, 48, 64]))
+    pk, table = to_pages(kp, kv, P, seed=idx)
+    pq, _ = to_pages(kq, kv, P, seed=idx)
+    pv, _ = to_pages(vd, kv, P, seed=idx)
+    assert torch.equal(dca.selfextend_decode_paged(qd.to(dev()), pk, pq, pv, table, kv, grp, win), od)
 
 
 @pytest.mark.parametrize("idx", range(N_CASES))
@@ -171,7 +180,15 @@ def test_sweep_coarse_fine_decode(idx):
     kg = k.to(dev())
     kp = _nan_tails(dca.rope_remap(kg, dca.DCA_MAP_PLAIN, 1, 0), kv)
     ks = _nan_tails(dca.coarse_fine_key_remap(kg, chunk, train, target), kv)
-    o = to_np(dca.coarse_fine_decode(qd.to(dev()), kp, ks, _nan_tails(v.to(dev()), kv), kv, chunk, train, target))
+    vd = _nan_tails(v.to(dev()), kv)
+    od = dca.coarse_fine_decode(qd.to(dev()), kp, ks, vd, kv, chunk, train, target)
+    o = to_np(od)
     O, _ = oracle.coarse_fine_decode_ref(qd, k, v, kv, chunk, train, target)
     for b in range(B):
         assert_close(o[b], O[b], dtype, f"coarse/fine decode seq {b}")
+    # the same rows from page pools: the same bits
+    P = int(rng.choice([16, 32, 48, 64]))
+    pk, table = to_pages(kp, kv, P, seed=idx)
+    ps, _ = to_pages(ks, kv, P, seed=idx)
+    pv, _ = to_pages(vd, kv, P, seed=idx)
+    assert torch.equal(dca.coarse_fine_decode_paged(qd.to(dev()), pk, ps, pv, table, kv, chunk, train, target), od)
