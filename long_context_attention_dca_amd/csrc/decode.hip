@@ -12,7 +12,8 @@
 //   2. split   : each wave streams one contiguous key range of one (batch,
 //                KV head) and keeps an online softmax for the GQA group's query
 //                heads (up to 32 per pass, the N side of a 32x32 MFMA).  K and
-//                V rows are read with fully coalesced 16-byte loads and stored
+//                V rows are read with fully coalesced 16-byte loads (with the
+//                non-temporal hint: each row is read once) and stored
 //                to a per-wave LDS slice as rows (K XOR-swizzled, V padded);
 //                the PV operand V^T is read back with the transposing LDS read
 //                of gfx950, so no 16-bit scatter stores are needed.  Partials
