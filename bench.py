@@ -85,7 +85,8 @@ class ClockSampler:
         self.path, self.power_path, self.samples, self.power, self.period = None, None, [], [], period_s
         self._stop, self._thread = threading.Event(), None
         try:
-            p = __import__("torch").cuda.get_device_properties(dev)
+            import torch
+            p = torch.cuda.get_device_properties(dev)
             base = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
             if os.access(base + "/pp_dpm_sclk", os.R_OK):
                 self.path = base + "/pp_dpm_sclk"
