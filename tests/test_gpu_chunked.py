@@ -147,3 +147,36 @@ def test_ragged_decode_100k_workload():
         Od, _ = oracle.dca_decode_ref(qd[b: b + 1], k[b: b + 1, : kv[b]], v[b: b + 1, : kv[b]], c, w, P["base"])
         mx, mean = assert_close(o[b], Od[0], torch.bfloat16, f"ragged decode seq {b}")
         log(f"  ragged decode seq {b} (kv_len {kv[b]}): max abs {mx:.3e}")
+
+
+def test_decode_more_sequences_than_one_launch_holds():
+    # Ragged decodes launch in groups of 64 sequences (their lengths travel in
+    # the kernel arguments): 70 sequences cross a group boundary.  Every row
+    # must equal the uniform decode of that sequence alone; a few are checked
+    # against the oracle too.  The same batch from page pools and under the
+    # SelfExtend map gives the same bits as its dense form.
+    B, cache_len, Hq, Hkv, D, c, w = 70, 300, 4, 2, 64, 128, 32
+    kv = [1 + (b * 37) % cache_len for b in range(B)]
+    qd, k, v = inputs.decode_inputs(B, cache_len, Hq, Hkv, D, "bf16", seed=304, qk_scale=2.0)
+    kc, vc = make_caches(k, v, kv, c, w)
+    o = dca.decode_varlen(qd.to(dev()), kc, vc, kv, c, w)
+    for b in range(B):
+        ou = dca.decode(qd[b: b + 1].to(dev()), kc[b: b + 1, : kv[b]].contiguous(),
+                        vc[b: b + 1, : kv[b]].contiguous(), c, w)
+        assert (ou[0].float() - o[b].float()).abs().max().item() <= 2e-2, b
+    got = to_np(o)
+    for b in (0, 63, 64, 69):
+        Od, _ = oracle.dca_decode_ref(qd[b: b + 1], k[b: b + 1, : kv[b]], v[b: b + 1, : kv[b]], c, w, 1e4)
+        assert_close(got[b], Od[0], torch.bfloat16, f"70 sequences, seq {b}")
+    from test_gpu_paged import to_pages
+    kp, table = to_pages(kc, kv, 16, seed=5)
+    vp, _ = to_pages(vc, kv, 16, seed=5)
+    assert torch.equal(dca.decode_paged(qd.to(dev()), kp, vp, table, kv, c, w), o)
+    kg = k.to(dev())
+    k_plain = dca.rope_remap(kg, dca.DCA_MAP_PLAIN, 1, 0)
+    k_grp = dca.rope_remap(kg, dca.DCA_MAP_SE_KEY_GROUPED, 4, 50)
+    se = dca.selfextend_decode(qd.to(dev()), k_plain, k_grp, vc, kv, 4, 50)
+    O, _ = oracle.selfextend_decode_ref(qd, k, v, kv, 4, 50)
+    sg = to_np(se)
+    for b in (0, 63, 64, 69):
+        assert_close(sg[b], O[b], torch.bfloat16, f"70 sequences selfextend, seq {b}")
