@@ -36,8 +36,11 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
-           "selfextend_prefill", "prefill_chunk", "decode_varlen", "coarse_fine_prefill", "prefill_workspace_bytes", "decode_workspace_bytes",
-           "selfextend_workspace_bytes", "decode_varlen_workspace_bytes", "DCAError", "library_path"]
+           "selfextend_prefill", "prefill_chunk", "decode_varlen", "decode_paged", "prefill_chunk_paged",
+           "coarse_fine_prefill", "selfextend_decode", "coarse_fine_decode", "selfextend_decode_paged",
+           "coarse_fine_decode_paged", "coarse_fine_key_remap", "prefill_workspace_bytes", "decode_workspace_bytes",
+           "selfextend_workspace_bytes", "decode_varlen_workspace_bytes", "coarse_fine_workspace_bytes",
+           "selfextend_decode_workspace_bytes", "coarse_fine_decode_workspace_bytes", "DCAError", "library_path"]
 
 _DT = {torch.float32: DCA_F32, torch.bfloat16: DCA_BF16}
 
@@ -530,3 +533,41 @@ def coarse_fine_prefill(q, k, v, chunk: int, train_len: int, target_len: int, ba
         chunk, train_len, target_len, float(base), float(sm_scale or 0.0), code,
         ws.data_ptr(), nbytes, _stream(q.device)))
     return (o, lse) if return_lse else o
+
+
+# ---- the C entry points under their own names (include/dca.h) ----------------------
+# The same marshalling functions as above: tensors in, the C call on torch's
+# current stream, tensors out.
+def dca_status_string(status: int) -> str:
+    return _lib.load().dca_status_string(int(status)).decode()
+
+
+def dca_version() -> int:
+    return int(_lib.load().dca_version())
+
+
+dca_rope_remap = rope_remap
+dca_prefill = prefill
+dca_prefill_prepare = prefill_prepare
+dca_prefill_attend = prefill_attend
+dca_prefill_workspace_bytes = prefill_workspace_bytes
+dca_decode = decode
+dca_decode_workspace_bytes = decode_workspace_bytes
+dca_selfextend_prefill = selfextend_prefill
+dca_selfextend_workspace_bytes = selfextend_workspace_bytes
+dca_prefill_chunk = prefill_chunk
+dca_decode_varlen = decode_varlen
+dca_decode_varlen_workspace_bytes = decode_varlen_workspace_bytes
+dca_decode_paged = decode_paged
+dca_prefill_chunk_paged = prefill_chunk_paged
+dca_coarse_fine_prefill = coarse_fine_prefill
+dca_coarse_fine_workspace_bytes = coarse_fine_workspace_bytes
+dca_selfextend_decode = selfextend_decode
+dca_selfextend_decode_workspace_bytes = selfextend_decode_workspace_bytes
+dca_coarse_fine_decode = coarse_fine_decode
+dca_coarse_fine_decode_workspace_bytes = coarse_fine_decode_workspace_bytes
+dca_selfextend_decode_paged = selfextend_decode_paged
+dca_coarse_fine_decode_paged = coarse_fine_decode_paged
+dca_coarse_fine_key_remap = coarse_fine_key_remap
+
+__all__ += [n for n in list(globals()) if n.startswith("dca_")]

@@ -35,6 +35,16 @@ def test_header_declarations_match_binding():
     assert declared_functions() == sorted(_lib.SIGNATURES)
 
 
+def test_python_binding_has_every_entry_point_by_name(lib):
+    # the binding exposes each C entry point under its own name (tensors in,
+    # the C call, tensors out)
+    import long_context_attention_dca_amd as dca
+    for name in declared_functions():
+        assert callable(getattr(dca, name, None)), name
+    assert dca.dca_version() == 10000
+    assert dca.dca_status_string(-3).startswith("DCA_ERR_WORKSPACE")
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
