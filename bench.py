@@ -16,6 +16,7 @@ Printed JSON (one line, stdout):
   roofline     the attention kernel against the bf16 dense MFMA peak
   decode       decode GB/s against the HBM peak
   rope_remap_100k  dca_rope_remap building the decode_100k key cache (GB/s)
+  prefill_16k_7b   the DCA prefill of the Llama2-7B-shaped 16k workload (32/32 heads)
   prefill_128k the same prefill at 131072 tokens
   cpu_baseline the fp64 oracle timed on a bounded sample of rows on the host
 """
@@ -188,6 +189,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-128k", action="store_true", help="skip the 131072-token prefill")
+    ap.add_argument("--no-7b", action="store_true", help="skip the Llama2-7B-shaped 16k prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-selfextend", action="store_true", help="skip the SelfExtend 32k prefill")
@@ -230,6 +232,8 @@ def main():
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode")
     run_128k = (args.only == "prefill128k") or (args.only is None and not args.no_128k)
+    P7 = inputs.WORKLOADS["llama2_7b_16k"]
+    run_7b = args.only is None and not args.no_7b
     SE = inputs.WORKLOADS["selfextend_70b_32k"]
     run_se = (args.only == "selfextend") or (args.only is None and not args.no_selfextend)
     CF = inputs.WORKLOADS["coarse_fine_70b_32k"]
@@ -562,6 +566,34 @@ def main():
                                 "prefill": {k_: CF[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "chunk",
                                                                   "train_len", "target_len")}}
         del cq, ck, cv, cws
+        torch.cuda.empty_cache()
+
+    # ---------------- Llama2-7B-shaped 16k prefill (reported beside the step) --
+    if run_7b:
+        log("generating llama2_7b_16k inputs")
+        q7h, k7h, v7h = inputs.prefill_inputs(P7["B"], P7["L"], P7["Hq"], P7["Hkv"], P7["D"], "bf16", P7["seed"])
+        q7, k7, v7 = q7h.to(dev), k7h.to(dev), v7h.to(dev)
+        del q7h, k7h, v7h
+        o7 = torch.empty_like(q7)
+        ws7 = torch.empty(dca.prefill_workspace_bytes(P7["B"], P7["L"], P7["Hkv"], P7["D"], P7["c"],
+                                                      torch.bfloat16), dtype=torch.uint8, device=dev)
+        for _ in range(max(1, args.warmup)):
+            prefill_step(q7, k7, v7, o7, ws7, P7, events(3))
+        torch.cuda.synchronize()
+        n7 = max(1, args.steps)
+        ev7 = [events(3) for _ in range(n7)]
+        for i in range(n7):
+            prefill_step(q7, k7, v7, o7, ws7, P7, ev7[i])
+        torch.cuda.synchronize()
+        prep = sum(e[0].elapsed_time(e[1]) for e in ev7) / n7
+        att = sum(e[1].elapsed_time(e[2]) for e in ev7) / n7
+        fl = prefill_flops(P7["B"], P7["L"], P7["Hq"], P7["D"])
+        result["prefill_16k_7b"] = {"ms": prep + att, "prepare_ms": prep, "attend_ms": att,
+                                    "tflops": fl / ((prep + att) * 1e-3) / 1e12,
+                                    "attend_tflops": fl / (att * 1e-3) / 1e12,
+                                    "frac": fl / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "steps": n7,
+                                    "shape": {k_: P7[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
+        del q7, k7, v7, o7, ws7
         torch.cuda.empty_cache()
 
     # ---------------- 128k prefill (reported beside the step) ----------------
