@@ -247,6 +247,11 @@ def main():
         o = torch.empty_like(q)
         nbytes = dca.prefill_workspace_bytes(P["B"], P["L"], P["Hkv"], P["D"], P["c"], torch.bfloat16)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        # setup: a prepare and a few attention calls on the fresh buffers
+        # (the first calls run slower), untimed
+        dca.prefill_prepare(k, v, P["c"], P["w"], P["base"], workspace=ws)
+        for _ in range(5):
+            dca.prefill_attend(q, ws, P["Hkv"], P["c"], P["w"], out=o)
     if run_decode:
         log("generating decode_100k inputs")
         dq_h, dk_h, dv_h = inputs.decode_inputs(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"], "bf16",
