@@ -29,8 +29,14 @@
  *   - GQA: Hq must be a multiple of Hkv; query head h reads KV head
  *     floor(h * Hkv / Hq) (contiguous groups).
  *   - Size limits: B, Hq and Hkv at most 65535 for the prefill entry points
- *     (Hq below 65536 for decode), sequence lengths below 2^30; a call
- *     outside them returns DCA_ERR_INVALID_ARG (the size queries return 0).
+ *     (Hq below 65536 for decode), sequence lengths below 2^30.  The prefill
+ *     entry points (whole, SelfExtend, coarse / fine, chunked) also need one
+ *     head's key rows, padded to a multiple of 128 rows, below 2^31 bytes:
+ *     round_up(L, 128) * D * element size < 2^31, i.e. L <= 2^23 - 128 for
+ *     bf16 at D = 128, 2^24 - 128 for bf16 at D = 64 (half of each for fp32);
+ *     for the chunked calls L is the largest pos0[b] + q_len[b].  A call
+ *     outside these limits returns DCA_ERR_INVALID_ARG (the size queries
+ *     return 0).
  *   - stream is a hipStream_t (NULL = the null stream).  Calls are
  *     asynchronous: a return of DCA_OK means "enqueued".  Device faults surface
  *     at the caller's next synchronisation.

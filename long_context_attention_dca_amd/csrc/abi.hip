@@ -24,10 +24,16 @@ bool head_dim_ok(int64_t D) { return D == 64 || D == 128; }
 int64_t elem_size(int dtype) { return dtype == DCA_F32 ? 4 : 2; }
 bool cw_ok(int c, int w) { return c >= 1 && c <= (1 << 24) && w >= 0 && w < c; }
 // Sizes of the prefill family: B and Hkv index grid dimensions limited to
-// 65535, and the padded K (or V) copy must stay far inside size_t.
+// 65535, and the padded K (or V) copy must stay far inside size_t.  One
+// head's padded key (or value) rows, Lp * D elements, must stay below 2^31
+// bytes: the attention kernel addresses a head through one buffer resource
+// whose record count and per-tile offsets are 32-bit (bf16 at D = 128: at
+// most 2^23 - 128 tokens; D = 64: 2^24 - 128).
 constexpr int64_t kMaxGridYZ = 65535;
-bool prefill_sizes_ok(int64_t B, int64_t L, int64_t Hkv, int64_t D) {
+constexpr int64_t kMaxHeadBytes = int64_t(1) << 31;
+bool prefill_sizes_ok(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype) {
   if (B > kMaxGridYZ || Hkv > kMaxGridYZ || L >= kMaxDim / 2) return false;
+  if (round_up(L, kPrefillRowAlign) * D * elem_size(dtype) >= kMaxHeadBytes) return false;
   return (double)B * (double)Hkv * (double)round_up(L, kPrefillRowAlign) * (double)D * 4.0 < 0x1p56;
 }
 bool base_ok(double base) { return base > 0.0 && isfinite(base); }
@@ -40,7 +46,7 @@ struct PrefillLayout {
 bool prefill_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c, int dtype,
                     PrefillLayout* out) {
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype) || c < 1) return false;
-  if (!prefill_sizes_ok(B, L, Hkv, D)) return false;
+  if (!prefill_sizes_ok(B, L, Hkv, D, dtype)) return false;
   PrefillLayout p;
   p.Lp = round_up(L, kPrefillRowAlign);
   const int64_t tbytes = (int64_t)c * (D / 2) * 16;
@@ -65,7 +71,7 @@ struct SeLayout {
 
 bool se_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int G, int W, int dtype, SeLayout* out) {
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype) || !se_ok(G, W)) return false;
-  if (!prefill_sizes_ok(B, L, Hkv, D)) return false;
+  if (!prefill_sizes_ok(B, L, Hkv, D, dtype)) return false;
   SeLayout p;
   p.Lp = round_up(L, kPrefillRowAlign);
   // largest position used: L - 1 (neighbor query) or the grouped query of row L - 1
@@ -357,7 +363,7 @@ struct CfLayout {
 
 static bool cf_layout(int64_t B, int64_t L, int64_t Hkv, int64_t D, int dtype, CfLayout* p) {
   if (B < 1 || L < 1 || Hkv < 1 || !head_dim_ok(D) || !dtype_ok(dtype)) return false;
-  if (!prefill_sizes_ok(B, L, Hkv, D)) return false;
+  if (!prefill_sizes_ok(B, L, Hkv, D, dtype)) return false;
   p->Lp = round_up(L, kPrefillRowAlign);
   const int64_t kbytes = round_up(B * Hkv * p->Lp * D * elem_size(dtype), 256);
   p->qtab = kThetaBytes;

@@ -83,6 +83,29 @@ def test_prefill_family_size_limits(lib):
     assert lib.dca_prefill_workspace_bytes(65535, (1 << 30) - 1, 65535, 128, 128, 1) == 0
 
 
+@pytest.mark.parametrize("D,dtype,limit", [(128, 1, 1 << 23), (64, 1, 1 << 24), (128, 0, 1 << 22),
+                                           (64, 0, 1 << 23)])
+def test_prefill_head_bytes_limit(lib, D, dtype, limit):
+    # One head's padded key rows (a multiple of 128 rows) must stay below 2^31
+    # bytes, so the attention kernel's 32-bit buffer offsets cannot wrap.
+    # The size queries return 0 from there on, and the calls refuse it before
+    # any HIP call; the largest accepted length is limit - 128.
+    ok, bad = limit - 128, limit - 127          # bad pads up to `limit` rows
+    for L in (ok,):
+        assert lib.dca_prefill_workspace_bytes(1, L, 1, D, 4096, dtype) > 0
+        assert lib.dca_selfextend_workspace_bytes(1, L, 1, D, 8, 1024, dtype) > 0
+        assert lib.dca_coarse_fine_workspace_bytes(1, L, 1, D, dtype) > 0
+    for L in (bad, limit, limit + 1000):
+        assert lib.dca_prefill_workspace_bytes(1, L, 1, D, 4096, dtype) == 0
+        assert lib.dca_selfextend_workspace_bytes(1, L, 1, D, 8, 1024, dtype) == 0
+        assert lib.dca_coarse_fine_workspace_bytes(1, L, 1, D, dtype) == 0
+        assert call_prefill(lib, L=L, D=D, dtype=dtype, Hq=1, Hkv=1, c=4096, w=1024,
+                            ws_bytes=1 << 62) == _lib.DCA_ERR_INVALID_ARG
+    # the chunked prefill counts the largest pos0 + q_len as the length
+    assert call_chunk(lib, pos0=(0, limit - 64), Lq=64, cache_len=limit, D=D, dtype=dtype,
+                      ws_bytes=1 << 62) == _lib.DCA_ERR_INVALID_ARG
+
+
 def test_decode_workspace_sizes(lib):
     n = lib.dca_decode_workspace_bytes(16, 100001, 64, 8, 128, 1)
     assert n > 16 * 64 * 3 * 128 * 2
