@@ -68,6 +68,22 @@ def _check(t: torch.Tensor, name: str, ndim: int, dtype=None) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_out(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    """A caller-supplied output: the kernels write exactly `shape` elements of
+    `dtype` on `device`, densely, so anything else is refused before the call
+    (a smaller buffer would be written past its end)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -99,8 +115,9 @@ def coarse_fine_workspace_bytes(B, L, Hkv, D, dtype) -> int:
 def _workspace(nbytes: int, device, workspace):
     if workspace is None:
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-    if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace must be a GPU buffer of at least {nbytes} bytes")
+    if (not isinstance(workspace, torch.Tensor) or workspace.device != torch.device(device)
+            or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < nbytes):
+        raise ValueError(f"workspace must be a contiguous buffer of at least {nbytes} bytes on {device}")
     return workspace
 
 
@@ -112,7 +129,7 @@ def rope_remap(x: torch.Tensor, map: int, c: int, w: int, base: float = 10000.0,
     _check(x, "x", 4)
     if out is None:
         out = torch.empty_like(x)
-    _check(out, "out", 4, x.dtype)
+    _check_out(out, "out", x.shape, x.dtype, x.device)
     B, L, H, D = x.shape
     _lib.check("dca_rope_remap", lib.dca_rope_remap(
         x.data_ptr(), out.data_ptr(), B, L, H, D, pos0, map, c, w, float(base), _dtype_code(x),
@@ -164,7 +181,7 @@ def prefill_prepare(k, v, c: int, w: int, base: float = 10000.0, workspace=None,
         raise ValueError("invalid prefill sizes")
     ws = _workspace(nbytes, k.device, workspace)
     if k_rot_out is not None:
-        _check(k_rot_out, "k_rot_out", 4, k.dtype)
+        _check_out(k_rot_out, "k_rot_out", k.shape, k.dtype, k.device)
     _lib.check("dca_prefill_prepare", lib.dca_prefill_prepare(
         k.data_ptr(), v.data_ptr(), _ptr(k_rot_out), B, L, Hkv, D, c, w, float(base), code,
         ws.data_ptr(), nbytes, _stream(k.device)))
@@ -179,12 +196,17 @@ def prefill_attend(q, workspace, Hkv: int, c: int, w: int, sm_scale: float | Non
     B, L, Hq, D = q.shape
     code = _dtype_code(q)
     o = torch.empty_like(q) if out is None else out
-    _check(o, "out", 4, q.dtype)
+    _check_out(o, "out", q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out(lse, "lse", (B, Hq, L), torch.float32, q.device)
     nbytes = int(lib.dca_prefill_workspace_bytes(B, L, Hkv, D, c, code))
+    if nbytes == 0:
+        raise ValueError("invalid prefill sizes")
+    if workspace.device != q.device or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a buffer of at least {nbytes} bytes on {q.device}")
     _lib.check("dca_prefill_attend", lib.dca_prefill_attend(
         q.data_ptr(), o.data_ptr(), _ptr(lse), B, L, Hq, Hkv, D, c, w, float(sm_scale or 0.0), code,
-        workspace.data_ptr(), min(nbytes, workspace.numel() * workspace.element_size()),
-        _stream(q.device)))
+        workspace.data_ptr(), nbytes, _stream(q.device)))
     return o
 
 
@@ -273,7 +295,7 @@ def prefill_chunk(q, k_cache, v_cache, pos0, c: int, w: int, base: float = 10000
     else:
         ql, qlv = _host_i64(q_len, B, "q_len")
     o = torch.zeros_like(q) if out is None else out
-    _check(o, "out", 4, q.dtype)
+    _check_out(o, "out", q.shape, q.dtype, q.device)
     lse = torch.full((B, Hq, Lq), float("-inf"), dtype=torch.float32, device=q.device) if return_lse else None
     max_keys = max(a + n for a, n in zip(p0v, qlv))
     nbytes = int(lib.dca_prefill_workspace_bytes(B, max(max_keys, 1), Hkv, D, c, code))
@@ -378,7 +400,7 @@ def prefill_chunk_paged(q, k_pages, v_pages, block_table, pos0, c: int, w: int, 
     else:
         ql, qlv = _host_i64(q_len, B, "q_len")
     o = torch.zeros_like(q) if out is None else out
-    _check(o, "out", 4, q.dtype)
+    _check_out(o, "out", q.shape, q.dtype, q.device)
     lse = torch.full((B, Hq, Lq), float("-inf"), dtype=torch.float32, device=q.device) if return_lse else None
     max_keys = max(a + n for a, n in zip(p0v, qlv))
     nbytes = int(lib.dca_prefill_workspace_bytes(B, max(max_keys, 1), Hkv, D, c, code))
@@ -501,7 +523,7 @@ def coarse_fine_key_remap(x, chunk: int, train_len: int, target_len: int, base: 
     _check(x, "x", 4)
     B, L, H, D = x.shape
     out = torch.empty_like(x) if out is None else out
-    _check(out, "out", 4, x.dtype)
+    _check_out(out, "out", x.shape, x.dtype, x.device)
     _lib.check("dca_coarse_fine_key_remap", lib.dca_coarse_fine_key_remap(
         x.data_ptr(), out.data_ptr(), B, L, H, D, int(pos0), chunk, train_len, target_len, float(base),
         _dtype_code(x), _stream(x.device)))
