@@ -17,10 +17,10 @@ Sources (cited by page title and section):
       Attention" and "2. Inter-Chunk Attention": the sequence is cut into
       fixed-size chunks; the relation of a pair is decided by the chunk-index
       difference (0 = intra, 1 = successive, >= 2 = inter); intra pairs keep
-      their exact unscaled distance; inter pairs keep the fine offset inside
+      their true distance with no scaling; inter pairs keep the fine offset inside
       the key's chunk and never exceed the pretrain window.
     - "Deep Dive", sub-section "1. Successive Chunk Smoothing": successive
-      pairs see the pure local distance near the chunk boundary and move
+      pairs see the plain local distance near the chunk edge and move
       continuously toward the inter-chunk value deeper into the chunk.
     - "End-to-End Implementation" script: causal pairs are those with i >= j
       (the diagonal included), and the effective distance over the causal

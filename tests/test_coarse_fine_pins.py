@@ -5,9 +5,10 @@ Source: "Dual-Chunk Attention: Training-Free 100k+ Context Guide", sections
 "End-to-End Implementation" script inspects (C = 512, L_train = 4096,
 L_target = 32768, kappa = 8).  Expected values below are worked out by hand
 from those formulas (the page prints the pairs but not the numbers), or are
-properties the page states: intra pairs unscaled, the ramp starting from the
-pure local distance at the chunk boundary, the fine offset keeping order
-inside the key's chunk, and no distance above L_train over a 16k horizon.
+properties the page states: intra pairs unscaled, the successive ramp
+beginning at the plain distance at the chunk edge, the fine offset keeping
+order inside the key's chunk, and no distance above L_train over a 16k
+horizon.
 """
 import math
 

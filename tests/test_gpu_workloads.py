@@ -4,7 +4,17 @@ benchmark times, on rows the oracle evaluates one by one.
 Rows: the chunk-geometry landmarks {0, 1, s-1, s, s+w-1, s+w, 2s-1, 2s,
 2s+w-1, 2s+w, c-1, c, L-1} plus 256 seeded random rows (128 at 131072
 tokens, on one query head per KV group).  Bars: bf16 max-abs
-<= 2e-2 and mean-abs <= 2e-3.
+<= 2e-2 and mean-abs <= 2e-3; LSE within the derived bf16 bar.
+
+At the configurations' own input scale (q, k ~ N(0, 1) / sqrt(D)) the
+softmax is close to uniform, and a wrong position map moves the output by
+less than bf16 rounding.  Each shape therefore also runs with q and k scaled
+to N(0, 1) * 2 (logits of standard deviation about 4, seed + 100), where the
+inter-chunk relation holds most long-range pairs ("Dual-Chunk Attention:
+Training-Free 100k+ Context Guide", "The Architecture" box and "Inter-Chunk
+Attention"), and reports the separation ratio: the distance of an oracle with
+a planted map mistake from the true oracle, over the GPU's distance from it.
+It must be at least 10.
 """
 import sys
 
@@ -13,12 +23,15 @@ import pytest
 import torch
 
 import oracle
+import oracle.dca_ref as ref
 import long_context_attention_dca_amd as dca
 from long_context_attention_dca_amd import inputs
+from test_gpu_parity import bf16_lse_bar
 
 pytestmark = pytest.mark.gpu
 
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+MIN_SEPARATION = 10.0
 
 
 def log(msg):
@@ -35,16 +48,47 @@ def landmark_rows(L, c, w, n_random, seed):
 
 
 def lse_bound_rows(q, k, rows, heads):
-    """bf16 LSE bar on the sampled rows: max(2e-2, 2^-8 * scale * |q_i| *
-    max_{j<=i} |k_j|).  Rounding the rotated q and k to bf16 moves every score
-    by at most 2^-8 * scale * |q| |k| (rotations keep norms), and the LSE by at
-    most the largest score change."""
+    """bf16 LSE bar (bf16_lse_bar) on the sampled rows: |q_i| and the largest
+    |k_j| over j <= i."""
     qn = torch.linalg.vector_norm(q[:, rows][:, :, heads], dim=-1, dtype=torch.float32).double().numpy()
     kn = torch.linalg.vector_norm(k, dim=-1, dtype=torch.float32).double().numpy()       # [B, L, Hkv]
     G = q.shape[2] // k.shape[2]
     kmax = np.maximum.accumulate(kn, axis=1)[:, rows][:, :, np.asarray(heads) // G]      # [B, R, H]
-    bound = 2.0 ** -8 / np.sqrt(q.shape[-1]) * qn * kmax
-    return np.maximum(2e-2, bound.transpose(0, 2, 1))                                    # [B, H, R]
+    return bf16_lse_bar(1.0 / np.sqrt(q.shape[-1]), qn, kmax).transpose(0, 2, 1)        # [B, H, R]
+
+
+# Planted map mistakes for the separation ratio (each is caught by the oracle
+# pins on tiny inputs as well).
+def _succ_as_inter(i, c, w):
+    """Successive pairs given the inter-chunk query position."""
+    a, _, e = _GOOD_QPOS(i, c, w)
+    return a, e, e
+
+
+def _succ_unsaturated(i, c, w):
+    """Successive query position s + (i mod s) without the cap at c - 1."""
+    a, _, e = _GOOD_QPOS(i, c, w)
+    s = c - w
+    return a, np.asarray(i, dtype=np.int64) % s + s, e
+
+
+_GOOD_QPOS = ref.query_positions
+
+
+def with_mutant(monkeypatch, fn, call):
+    monkeypatch.setattr(ref, "query_positions", fn)
+    try:
+        return call()
+    finally:
+        monkeypatch.setattr(ref, "query_positions", _GOOD_QPOS)
+
+
+def separation(got, want, wrong, what):
+    ratio = np.linalg.norm(wrong - want) / max(np.linalg.norm(got - want), 1e-30)
+    log(f"  {what}: separation ratio {ratio:.1f} (wrong-map distance {np.linalg.norm(wrong - want):.3e}, "
+        f"GPU distance {np.linalg.norm(got - want):.3e})")
+    assert ratio >= MIN_SEPARATION, (what, ratio)
+    return ratio
 
 
 def check(got, want, what):
@@ -54,10 +98,11 @@ def check(got, want, what):
     assert mx <= BF16_MAX and mean <= BF16_MEAN, what
 
 
-def run_prefill_workload(name, heads=None, n_random=256, qk_scale=None, seed_offset=0):
+def run_prefill_workload(name, heads=None, n_random=256, qk_scale=None, seed_offset=0, mutant=None,
+                         monkeypatch=None):
     cfg = inputs.WORKLOADS[name]
     B, L, Hq, Hkv, D, c, w = (cfg[k] for k in ("B", "L", "Hq", "Hkv", "D", "c", "w"))
-    log(f"[{name}] generating inputs (seed {cfg['seed'] + seed_offset})")
+    log(f"[{name}] generating inputs (seed {cfg['seed'] + seed_offset}, qk scale {qk_scale})")
     q, k, v = inputs.prefill_inputs(B, L, Hq, Hkv, D, cfg["dtype"], seed=cfg["seed"] + seed_offset,
                                     qk_scale=qk_scale)
     log(f"[{name}] GPU prefill")
@@ -73,19 +118,34 @@ def run_prefill_workload(name, heads=None, n_random=256, qk_scale=None, seed_off
     O, LSE = oracle.dca_prefill_ref(q, k, v, c, w, cfg["base"], rows=rows, heads=heads)
     check(og, O, f"{name} O")
     lerr = np.abs(lg - LSE)
-    assert np.all(lerr <= lse_bound_rows(q, k, torch.from_numpy(rows), torch.from_numpy(heads))), lerr.max()
+    bar = lse_bound_rows(q, k, torch.from_numpy(rows), torch.from_numpy(heads))
+    log(f"  {name} LSE: max abs {lerr.max():.3e} (bar at that element {bar.flat[lerr.argmax()]:.3e}, "
+        f"smallest bar {bar.min():.3e})")
+    assert np.all(lerr <= bar), lerr.max()
+    if mutant is not None:
+        log(f"[{name}] oracle with a planted map mistake ({mutant.__name__})")
+        Ow = with_mutant(monkeypatch, mutant, lambda: oracle.dca_prefill_ref(
+            q, k, v, c, w, cfg["base"], rows=rows, heads=heads)[0])
+        separation(og, O, Ow, f"{name} vs {mutant.__name__}")
 
 
 def test_llama2_7b_16k_sampled_rows():
     run_prefill_workload("llama2_7b_16k")
 
 
-def test_llama2_7b_16k_discriminating_inputs():
-    run_prefill_workload("llama2_7b_16k", heads=[0, 9, 31], qk_scale=2.0, seed_offset=100)
+def test_llama2_7b_16k_discriminating_inputs(monkeypatch):
+    run_prefill_workload("llama2_7b_16k", heads=[0, 9, 31], qk_scale=2.0, seed_offset=100,
+                         mutant=_succ_as_inter, monkeypatch=monkeypatch)
 
 
 def test_llama2_70b_32k_sampled_rows():
     run_prefill_workload("llama2_70b_32k")
+
+
+def test_llama2_70b_32k_discriminating_inputs(monkeypatch):
+    # one query head per KV group, each at another position inside its group
+    run_prefill_workload("llama2_70b_32k", heads=[g * 8 + g % 8 for g in range(8)], qk_scale=2.0,
+                         seed_offset=100, mutant=_succ_as_inter, monkeypatch=monkeypatch)
 
 
 def test_llama2_70b_128k_sampled_rows():
@@ -93,11 +153,17 @@ def test_llama2_70b_128k_sampled_rows():
     run_prefill_workload("llama2_70b_128k", heads=[g * 8 + (g % 8) for g in range(8)], n_random=128)
 
 
-def test_decode_100k_sampled_batches():
+def test_llama2_70b_128k_discriminating_inputs(monkeypatch):
+    run_prefill_workload("llama2_70b_128k", heads=[g * 8 + (7 - g) for g in range(8)], n_random=64,
+                         qk_scale=2.0, seed_offset=100, mutant=_succ_as_inter, monkeypatch=monkeypatch)
+
+
+def run_decode_workload(qk_scale=None, seed_offset=0, mutant=None, monkeypatch=None):
     cfg = inputs.WORKLOADS["decode_100k"]
     B, kv_len, Hq, Hkv, D, c, w = (cfg[k] for k in ("B", "kv_len", "Hq", "Hkv", "D", "c", "w"))
-    log("[decode_100k] generating inputs")
-    q, k, v = inputs.decode_inputs(B, kv_len, Hq, Hkv, D, cfg["dtype"], seed=cfg["seed"])
+    log(f"[decode_100k] generating inputs (seed {cfg['seed'] + seed_offset}, qk scale {qk_scale})")
+    q, k, v = inputs.decode_inputs(B, kv_len, Hq, Hkv, D, cfg["dtype"], seed=cfg["seed"] + seed_offset,
+                                   qk_scale=qk_scale)
     log("[decode_100k] building the rotated cache and decoding")
     kc = dca.rope_remap(k.cuda(), dca.DCA_MAP_KEY, c, w, cfg["base"], 0)
     vg = v.cuda()
@@ -111,4 +177,26 @@ def test_decode_100k_sampled_batches():
     log(f"[decode_100k] oracle on batches {batches}")
     O, LSE = oracle.dca_decode_ref(q, k, v, c, w, cfg["base"], batches=batches)
     check(og[batches], O, "decode_100k O")
-    assert np.abs(lg[batches] - LSE).max() <= 2e-2
+    qn = torch.linalg.vector_norm(q[batches], dim=-1, dtype=torch.float32).double().numpy()   # [b, Hq]
+    kmax = torch.linalg.vector_norm(k[batches], dim=-1, dtype=torch.float32).amax(dim=1).double().numpy()
+    bar = bf16_lse_bar(1.0 / np.sqrt(D), qn, np.repeat(kmax, Hq // Hkv, axis=1))
+    lerr = np.abs(lg[batches] - LSE)
+    log(f"  decode_100k LSE: max abs {lerr.max():.3e} (smallest bar {bar.min():.3e})")
+    assert np.all(lerr <= bar), lerr.max()
+    if mutant is not None:
+        log(f"[decode_100k] oracle with a planted map mistake ({mutant.__name__})")
+        Ow = with_mutant(monkeypatch, mutant, lambda: oracle.dca_decode_ref(
+            q, k, v, c, w, cfg["base"], batches=batches)[0])
+        separation(og[batches], O, Ow, f"decode_100k vs {mutant.__name__}")
+
+
+def test_decode_100k_sampled_batches():
+    run_decode_workload()
+
+
+def test_decode_100k_discriminating_inputs(monkeypatch):
+    # The new token sits at 100000, 1696 past the start of its chunk (>= w), so
+    # its successive position is already the inter one (c - 1) and treating
+    # successive pairs as inter changes nothing here; the planted mistake is
+    # the successive position left uncapped (s + 1696 = 4768 > c - 1).
+    run_decode_workload(qk_scale=2.0, seed_offset=100, mutant=_succ_unsaturated, monkeypatch=monkeypatch)
