@@ -43,7 +43,9 @@
  *   - Argument validation happens before any HIP call, so an invalid call
  *     returns its error without touching the device.  No C++ exception
  *     crosses this interface.  Calls on different streams with distinct
- *     workspaces are independent; the library keeps no global state.
+ *     workspaces are independent; the library keeps no global state, except
+ *     the static scratch of dca_decode_paged_noalloc (one array per GPU) and
+ *     the device address of each GPU's copy of it.
  */
 #ifndef DCA_H_
 #define DCA_H_
@@ -77,6 +79,12 @@ extern "C" {
 #define DCA_ERR_UNSUPPORTED (-2) /* head dim or dtype the kernels do not implement               */
 #define DCA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the query returned          */
 #define DCA_ERR_HIP (-4)         /* a HIP launch reported an error                                */
+#define DCA_ERR_TOO_LARGE (-5)   /* dca_decode_paged_noalloc: the call needs more scratch than
+                                    DCA_NOALLOC_SCRATCH_BYTES                                    */
+
+/* Bytes of the static device scratch that dca_decode_paged_noalloc uses
+ * (one copy per GPU, held until the process ends). */
+#define DCA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* dca_status_string(int status);
@@ -363,6 +371,33 @@ int dca_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pa
                             int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv, int64_t D,
                             int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * dca_decode_paged_noalloc - dca_decode_paged without a workspace argument,
+ * for callers that cannot allocate device memory: code recorded into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus ws / ws_bytes), same kernels and bit-identical
+ * results as dca_decode_paged.  The scratch the decode needs (rotated query
+ * variants and the per-key-range partial O / LSE, the size
+ * dca_decode_varlen_workspace_bytes(kv_len, B, Hq, Hkv, D, dtype) reports)
+ * comes from a static device array of DCA_NOALLOC_SCRATCH_BYTES (32 MiB) in
+ * the library; a call needing more returns DCA_ERR_TOO_LARGE before touching
+ * the device (e.g. B * Hq * (key ranges) * D * 4 bytes of partials: the
+ * 16 x 64-head, 100k-token decode needs about 9 MiB).  The call allocates
+ * nothing (no hipMalloc / hipFree, no host-side allocation for DCA); the
+ * first call on a device looks up that device's copy of the array with
+ * hipGetSymbolAddress.  The array is shared by every call on the same GPU
+ * and keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that overlap on one GPU (on different streams, or from several host
+ * threads) race on it and must be serialised by the caller.  The current
+ * device must be the one that holds the tensors.
+ */
+int dca_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                             const int32_t* block_table, void* o, float* lse, const int64_t* kv_len,
+                             int64_t B, int64_t num_pages, int64_t page_size, int64_t max_blocks,
+                             int64_t Hq, int64_t Hkv, int64_t D, int c, int w, double rope_base,
+                             float sm_scale, int dtype, void* stream);
 
 /*
  * Decode under the SelfExtend and coarse / fine maps.

@@ -32,11 +32,11 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     DCA_BF16, DCA_F32, DCA_MAP_KEY, DCA_MAP_PLAIN, DCA_MAP_Q_INTER, DCA_MAP_Q_INTRA,
-    DCA_MAP_Q_SUCC, DCA_MAP_SE_KEY_GROUPED, DCA_MAP_SE_Q_GROUPED, DCAError,
+    DCA_MAP_Q_SUCC, DCA_MAP_SE_KEY_GROUPED, DCA_MAP_SE_Q_GROUPED, DCA_NOALLOC_SCRATCH_BYTES, DCAError,
 )
 
 __all__ = ["rope_remap", "prefill", "prefill_prepare", "prefill_attend", "decode",
-           "selfextend_prefill", "prefill_chunk", "decode_varlen", "decode_paged", "prefill_chunk_paged",
+           "selfextend_prefill", "prefill_chunk", "decode_varlen", "decode_paged", "decode_paged_noalloc", "prefill_chunk_paged",
            "coarse_fine_prefill", "selfextend_decode", "coarse_fine_decode", "selfextend_decode_paged",
            "coarse_fine_decode_paged", "coarse_fine_key_remap", "prefill_workspace_bytes", "decode_workspace_bytes",
            "selfextend_workspace_bytes", "decode_varlen_workspace_bytes", "coarse_fine_workspace_bytes",
@@ -382,6 +382,32 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_len, c: int, w: int, base:
     return (o, lse) if return_lse else o
 
 
+def decode_paged_noalloc(q, k_pages, v_pages, block_table, kv_len, c: int, w: int, base: float = 10000.0,
+                         sm_scale: float | None = None, out=None, lse=None):
+    """decode_paged without a workspace: the library keeps the decode's scratch in a
+    static device buffer of DCA_NOALLOC_SCRATCH_BYTES per GPU (calls that overlap on
+    one GPU race on it).  Pass `out` (and `lse`) to make the call allocate nothing;
+    they are allocated here when None.  Returns out (and lse when given)."""
+    lib = _lib.load()
+    _check(q, "q", 3)
+    num_pages, page_size, Hkv, max_blocks = _check_pages(k_pages, v_pages, block_table, q)
+    B, Hq, D = q.shape
+    if k_pages.shape[3] != D or block_table.shape[0] != B:
+        raise ValueError("page pool / block table shapes do not match q")
+    code = _dtype_code(q)
+    kl, _ = _host_i64(kv_len, B, "kv_len")
+    o = torch.empty_like(q) if out is None else out
+    _check_out(o, "out", q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out(lse, "lse", (B, Hq), torch.float32, q.device)
+    with torch.cuda.device(q.device):   # the scratch used is the current device's
+        _lib.check("dca_decode_paged_noalloc", lib.dca_decode_paged_noalloc(
+            q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), o.data_ptr(),
+            _ptr(lse), kl, B, num_pages, page_size, max_blocks, Hq, Hkv, D, c, w, float(base),
+            float(sm_scale or 0.0), code, _stream(q.device)))
+    return o if lse is None else (o, lse)
+
+
 def prefill_chunk_paged(q, k_pages, v_pages, block_table, pos0, c: int, w: int, base: float = 10000.0,
                         sm_scale: float | None = None, q_len=None, return_lse: bool = False, out=None,
                         workspace=None):
@@ -581,6 +607,7 @@ dca_prefill_chunk = prefill_chunk
 dca_decode_varlen = decode_varlen
 dca_decode_varlen_workspace_bytes = decode_varlen_workspace_bytes
 dca_decode_paged = decode_paged
+dca_decode_paged_noalloc = decode_paged_noalloc
 dca_prefill_chunk_paged = prefill_chunk_paged
 dca_coarse_fine_prefill = coarse_fine_prefill
 dca_coarse_fine_workspace_bytes = coarse_fine_workspace_bytes

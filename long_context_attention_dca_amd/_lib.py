@@ -22,6 +22,8 @@ DCA_ERR_INVALID_ARG = -1
 DCA_ERR_UNSUPPORTED = -2
 DCA_ERR_WORKSPACE = -3
 DCA_ERR_HIP = -4
+DCA_ERR_TOO_LARGE = -5
+DCA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _i64, _int, _dbl, _flt, _vp, _sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float,
                                     ctypes.c_void_p, ctypes.c_size_t)
@@ -56,6 +58,8 @@ SIGNATURES = {
                           _flt, _int, _vp, _sz, _vp]),
     "dca_decode_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
+    "dca_decode_paged_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                        _i64, _int, _int, _dbl, _flt, _int, _vp]),
     "dca_prefill_chunk_paged": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64p, _i64p, _i64, _i64, _i64, _i64,
                                        _i64, _i64, _i64, _i64, _int, _int, _dbl, _flt, _int, _vp, _sz, _vp]),
     "dca_selfextend_decode_workspace_bytes": (_sz, [_i64p, _i64, _i64, _i64, _i64, _int, _int, _int]),

@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <vector>
 
 #include "dca.h"
@@ -129,6 +130,8 @@ const char* dca_status_string(int status) {
       return "DCA_ERR_WORKSPACE: workspace missing, misaligned or smaller than the size query";
     case DCA_ERR_HIP:
       return "DCA_ERR_HIP: a HIP launch reported an error";
+    case DCA_ERR_TOO_LARGE:
+      return "DCA_ERR_TOO_LARGE: the call needs more scratch than the library's static buffer holds";
     default:
       return "unknown DCA status";
   }
@@ -636,7 +639,10 @@ bool map_decode_layout(const int64_t* kv_len, int64_t B, int64_t Hq, int64_t Hkv
 int decode_varlen_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                        const int64_t* kv_len, int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv,
                        int64_t D, int c, int w, double rope_base, float sm_scale, int dtype, void* ws,
-                       size_t ws_bytes, void* stream, const PagedKv& pg, const DecodeMap& dm = DecodeMap{}) {
+                       size_t ws_bytes, void* stream, const PagedKv& pg, const DecodeMap& dm = DecodeMap{},
+                       size_t* need_bytes = nullptr) {
+  // need_bytes non-null: validate every argument, store the scratch bytes the
+  // call needs and return without touching the device.
   if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !o || !kv_len) return DCA_ERR_INVALID_ARG;
   if (B < 1 || cache_len < 1 || cache_len >= kMaxDim / 2 || Hq < 1 || Hkv < 1 || Hq % Hkv)
@@ -654,6 +660,10 @@ int decode_varlen_impl(const void* q, const void* k_cache, const void* v_cache, 
   DecodeLayout p;
   std::vector<int64_t> seg;
   if (!map_decode_layout(kv_len, B, Hq, Hkv, D, dtype, dm, &p, &seg)) return DCA_ERR_INVALID_ARG;
+  if (need_bytes) {
+    *need_bytes = p.total;
+    return DCA_OK;
+  }
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
   uint8_t* base = (uint8_t*)ws;
   const int64_t es = elem_size(dtype);
@@ -715,6 +725,35 @@ bool paged_ok(const int32_t* block_table, int64_t B, int64_t num_pages, int64_t 
   return true;
 }
 
+// ---- scratch for the entry point that allocates nothing ------------------------
+// dca_decode_paged_noalloc keeps the decode's partial results (rotated query
+// variants, per-range O and LSE) in this file-scope device array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names only a
+// host-side stand-in, so kernels are handed the device address that
+// hipGetSymbolAddress returns, taken once per device (with that device
+// current) and kept here.
+constexpr size_t kScratchBytes = DCA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxScratchDevices];
+
+// Device address of the current device's scratch array (set up on the first
+// call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return DCA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DCA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DCA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -762,6 +801,30 @@ int dca_decode_paged(const void* q, const void* k_pages, const void* v_pages, co
   if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
   return decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, max_blocks * page_size, Hq, Hkv, D, c, w,
                             rope_base, sm_scale, dtype, ws, ws_bytes, stream, pg);
+}
+
+int dca_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                             void* o, float* lse, const int64_t* kv_len, int64_t B, int64_t num_pages,
+                             int64_t page_size, int64_t max_blocks, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
+                             double rope_base, float sm_scale, int dtype, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(D)) return DCA_ERR_UNSUPPORTED;
+  PagedKv pg;
+  if (!paged_ok(block_table, B, num_pages, page_size, max_blocks, &pg)) return DCA_ERR_INVALID_ARG;
+  // Every argument is checked, and the scratch the call needs sized, before
+  // the first HIP call.
+  size_t need = 0;
+  const int64_t cache_len = max_blocks * page_size;
+  int r = decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, cache_len, Hq, Hkv, D, c, w, rope_base,
+                             sm_scale, dtype, nullptr, 0, stream, pg, DecodeMap{}, &need);
+  if (r != DCA_OK) return r;
+  if (need > kScratchBytes) return DCA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  r = scratch_address(&ws);
+  if (r != DCA_OK) return r;
+  // The kernels write every partial they later read (no part of the scratch
+  // has to start at zero).
+  return decode_varlen_impl(q, k_pages, v_pages, o, lse, kv_len, B, cache_len, Hq, Hkv, D, c, w, rope_base,
+                            sm_scale, dtype, ws, kScratchBytes, stream, pg);
 }
 
 

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.dca_status_string(code).decode().startswith("DCA_")
     assert lib.dca_status_string(12345).decode() == "unknown DCA status"
     assert lib.dca_version() == 10000
@@ -349,6 +349,34 @@ def test_decode_paged_validation(lib):
         a = list(ok)
         a[i] = bad
         assert lib.dca_decode_paged(*a) == st, (i, bad)
+
+
+def test_decode_paged_noalloc_validation(lib):
+    # Same arguments as dca_decode_paged without (ws, ws_bytes).  Invalid calls,
+    # and calls that need more than the static scratch, return before any HIP
+    # call (the fake pointers are never touched).
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(40, 100), 2, 20, 16, 8, 8, 2, 64, 128, 32, 1e4, 0.0, 1, None]
+    for i, bad, st in [(3, None, -1), (0, None, -1), (4, None, -1), (9, 8, -1), (8, 0, -1),
+                       (6, _i64s(40, 129), -1), (6, None, -1), (13, 96, -2), (18, 3, -2), (15, 128, -1),
+                       (0, FAKE + 8, -1)]:
+        a = list(ok)
+        a[i] = bad
+        assert lib.dca_decode_paged_noalloc(*a) == st, (i, bad)
+    # 64 sequences x 1024 query heads: the rotated query variants alone take
+    # 64 * 1024 * 3 * 128 * 2 bytes > 32 MiB
+    big = [FAKE, FAKE, FAKE, FAKE, FAKE, None, _i64s(*([1000] * 64)), 64, 4096, 16, 64, 1024, 8, 128, 4096,
+           1024, 1e4, 0.0, 1, None]
+    need = lib.dca_decode_varlen_workspace_bytes(_i64s(*([1000] * 64)), 64, 1024, 8, 128, 1)
+    assert need > _lib.DCA_NOALLOC_SCRATCH_BYTES
+    assert lib.dca_decode_paged_noalloc(*big) == _lib.DCA_ERR_TOO_LARGE
+    assert lib.dca_status_string(_lib.DCA_ERR_TOO_LARGE).decode().startswith("DCA_ERR_TOO_LARGE")
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DCA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DCA_NOALLOC_SCRATCH_BYTES
+    assert "#define DCA_ERR_TOO_LARGE (-5)" in text and _lib.DCA_ERR_TOO_LARGE == -5
 
 
 def test_prefill_chunk_paged_validation(lib):
