@@ -34,8 +34,6 @@ constexpr int SUB = 32;  // keys per wave sub-tile
 constexpr int kMaxSplits = 1024;  // partials merged per query head
 
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ inline bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
-__device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int NCK>
 __device__ inline int swz(int row, int chunk) {
@@ -367,13 +365,9 @@ decode_split_bf16_kernel(DecodeArgs a, int nqg, float scale_log2) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u * 8 + e], scale_log2, -m_run));
-        const uint4 pu = pack_bf16x8(p);
-        // Row sum of the bf16-rounded probabilities: the values PV multiplies.
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, lsum, false);
-        const bf16x8 pf = as_bf16x8(pu);
+        // Row sum of the fp32 probabilities (as the prefill kernels sum them).
+        lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        const bf16x8 pf = as_bf16x8(pack_bf16x8(p));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const uint2 lo = tr_read(vtb, u * 16 * VROWB + db * 64);

@@ -36,6 +36,8 @@
 //   * Workgroups are ordered longest causal row first, and, when B*Hkv is a
 //     multiple of 8, mapped so that each XCD (workgroup id mod 8) serves whole
 //     GQA groups and their K/V stay in that XCD's L2.
+#include <type_traits>
+
 #include "dca_common.hpp"
 #include "dca_launch.hpp"
 
@@ -357,9 +359,11 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 // matrix core while the other runs the softmax (the hardware co-issues them;
 // measured 4% faster than four independent waves per workgroup, and raising
 // the MFMA wave's priority made it slower).  Phases end at a workgroup
-// barrier.  K(t+1) and V(t) are loaded straight into LDS at the
-// start of phase 2t and waited for at the end of phase 2t+1; K and V are each
-// double-buffered.  With s a multiple of TK every 32-row wave block lies in
+// barrier.  K(t+1) and V(t) are loaded straight into LDS by group 0, one
+// load every few MFMAs of its phase 2t, and waited for at the end of phase
+// 2t+1; K and V are each double-buffered.  The softmax row sums add fp32
+// probabilities with plain VALU adds (the bf16 dot2 instructions wait for the
+// matrix pipe and would queue behind the other group's MFMAs).  With s a multiple of TK every 32-row wave block lies in
 // one chunk and every key tile in one chunk, so a (wave, tile) pair has a
 // single relation and no straddle handling is needed.
 // Maximum of a lane's 32 scores as a tree of max3 (depth 4), so the wave is
@@ -416,7 +420,15 @@ constexpr int kBufferWord3 = 0x00020000;
 // workgroup barrier.  Written as asm (with a compiler memory clobber) so the
 // compiler adds no wait on the direct-to-LDS loads still in flight, whose
 // data is only needed two phases later.
-__device__ inline void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The scheduling barriers keep the compiler from moving any instruction
+// across the phase boundary: MFMAs of an X phase sunk into the next phase
+// would wait behind the other group's MFMA chain on the shared matrix pipe,
+// and the softmax that needs their results with them.
+__device__ inline void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int D, int MAP, int NSUB>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -557,27 +569,54 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     }
   };
 
-  // ---- direct-to-LDS staging, 1-KiB pieces round-robin over the 8 waves -----
-  constexpr int KPW = (SM::KPIECES + 7) / 8;
-  constexpr int VPW = (SM::VPIECES + 7) / 8;
-  uint32_t koff[KPW], voff[VPW];
+  // ---- direct-to-LDS staging ----------------------------------------------------
+  // Group 0's four waves issue every 1-KiB piece of the tiles: K(t+1) and V(t)
+  // are spread through the MFMA chain of their X(t) phase, one load every few
+  // MFMAs.  (Issued at once by all eight waves at the start of a tile, the 70
+  // loads of a 128-key tile queued in the load path for 700-1250 cycles and
+  // held up the start of that phase for both groups.)  A wave with one piece
+  // fewer than the others issues its last piece twice (the same bytes to the
+  // same place), so every wave's chain has the same shape.
+  constexpr int KPW = (SM::KPIECES + 3) / 4;   // K loads per group-0 wave and tile
+  constexpr int VPW = (SM::VPIECES + 3) / 4;   // V loads per sub-tile and group-0 wave
+  constexpr int NLOAD = KPW + NSUB * VPW;      // loads per group-0 wave and tile
+  const int lw = wave & 3;
+  auto kpiece = [&](int i) __attribute__((always_inline)) {
+    const int p = lw + 4 * i;
+    return p < SM::KPIECES ? p : p - 4;
+  };
+  auto vpiece = [&](int i) __attribute__((always_inline)) {
+    const int p = lw + 4 * i;
+    return p < SM::VPIECES ? p : p - 4;
+  };
+  // Per-lane source offsets inside a tile (K below 32 KiB, a V sub-tile
+  // below 16 KiB), two 16-bit offsets per register.
+  static_assert(SM::KPIECES * 1024 <= 65536 && SM::VSUB <= 65536, "offsets must fit in 16 bits");
+  uint32_t koff2[(KPW + 1) / 2], voff2[(VPW + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (KPW + 1) / 2; ++i) koff2[i] = 0;
+#pragma unroll
+  for (int i = 0; i < (VPW + 1) / 2; ++i) voff2[i] = 0;
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
-    const int byte = (wave + 8 * i) * 1024 + lane * 16;
+    const int byte = kpiece(i) * 1024 + lane * 16;
     const int row = byte / SM::KROW, w = byte % SM::KROW;
-    koff[i] = (uint32_t)(row * D * 2 + (w < D * 2 ? w : 0));
+    koff2[i >> 1] |= (uint32_t)(row * D * 2 + (w < D * 2 ? w : 0)) << (16 * (i & 1));
   }
 #pragma unroll
   for (int i = 0; i < VPW; ++i) {
-    const int byte = (wave + 8 * i) * 1024 + lane * 16;
+    const int byte = vpiece(i) * 1024 + lane * 16;
     const int row = byte / SM::VROW, w = byte % SM::VROW;
-    voff[i] = (uint32_t)(row * 64 * 2 + (w < 64 * 2 ? w : 0));
+    voff2[i >> 1] |= (uint32_t)(row * 64 * 2 + (w < 64 * 2 ? w : 0)) << (16 * (i & 1));
   }
+  auto koff = [&](int i) __attribute__((always_inline)) { return (koff2[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
+  auto voff = [&](int i) __attribute__((always_inline)) { return (voff2[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
   // K/V tiles go straight to LDS through buffer loads (MUBUF with the lds
-  // bit).  The descriptor covers this head's Lp rows exactly (Lp is a
-  // multiple of the widest tile, so no tile reaches past it).  The FLAT form
-  // of the same DMA would make the compiler wait for every outstanding LDS
-  // read (lgkmcnt(0)) while it is in flight.
+  // bit).  The descriptor covers this head's Lp rows exactly; a load past them
+  // (the K tile after the last one, which the last X phase issues and nothing
+  // reads) returns zeros.  The FLAT form of the same DMA would make the
+  // compiler wait for every outstanding LDS read (lgkmcnt(0)) while it is in
+  // flight.
   const uint32_t head_bytes = (uint32_t)((int64_t)a.Lp * D * 2);
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, kBufferWord3);
@@ -586,32 +625,32 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   if constexpr (MAP != kMapDCA)
     krsrc2 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint16_t*)a.krot2 + bg * (int64_t)a.Lp * D), (short)0, head_bytes, kBufferWord3);
-  auto issue_k = [&](int t) {
-    const int soff = tile_of(t) * TK * D * 2;
-    uint8_t* dst = smem + KB0 + (t & 1) * SM::KBYTES;
+  // K piece slot i of virtual tile tk
+  auto load_k = [&](int tk, int i) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)tile_of(tk) * (uint32_t)(TK * D * 2);
     __amdgpu_buffer_rsrc_t rs = krsrc;
     if constexpr (MAP == kMapSelfExtend)
-      if (class_of(t) == kSeGrouped) rs = krsrc2;
+      if (class_of(tk) == kSeGrouped) rs = krsrc2;
     if constexpr (MAP == kMapCoarseFine)
-      if (t < n_gr) rs = krsrc2;   // the scaled-key pass (same for every wave)
-#pragma unroll
-    for (int i = 0; i < KPW; ++i)
-      if (wave + 8 * i < SM::KPIECES)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
-                                                 16, (int)koff[i], soff, 0, 0);
+      if (tk < n_gr) rs = krsrc2;   // the scaled-key pass (same for every wave)
+    uint8_t* dst = smem + KB0 + (tk & 1) * SM::KBYTES + kpiece(i) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, (int)koff(i),
+                                             (int)soff, 0, 0);
   };
-  // V: NSUB consecutive 64-key tiles of the HBM layout.
-  auto issue_v = [&](int t) {
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int soff = (tile_of(t) * NSUB + sub) * 64 * D * 2;
-      uint8_t* dst = smem + VB0 + (t & 1) * SM::VBYTES + sub * SM::VSUB;
-#pragma unroll
-      for (int i = 0; i < VPW; ++i)
-        if (wave + 8 * i < SM::VPIECES)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * i) * 1024),
-                                                   16, (int)voff[i], soff, 0, 0);
-    }
+  // V piece slot i of sub-tile sub of virtual tile t (NSUB consecutive 64-key
+  // tiles of the HBM layout)
+  auto load_v = [&](int t, int sub, int i) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)(tile_of(t) * NSUB + sub) * (uint32_t)(64 * D * 2);
+    uint8_t* dst = smem + VB0 + (t & 1) * SM::VBYTES + sub * SM::VSUB + vpiece(i) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)dst, 16, (int)voff(i),
+                                             (int)soff, 0, 0);
+  };
+  // load slot s of X(t): K(t+1) pieces first, then V(t)
+  auto load_slot = [&](int t, int s) __attribute__((always_inline)) {
+    if (s < KPW)
+      load_k(t + 1, s);
+    else
+      load_v(t, (s - KPW) / VPW, (s - KPW) % VPW);
   };
   const int kfrag = ql * SM::KROW + hh * 16;
   const int vfrag = ql * SM::VROW + hh * 16;
@@ -691,20 +730,25 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     // running max is the sentinel) sends the wave through the exact rescale:
     // the true max, the accumulator rescale and the exps again.  Every stored
     // probability is therefore at most 2^8 and O and l share one max.
+    // The row sum adds the fp32 probabilities with plain VALU adds: the
+    // bf16 dot2 instructions wait for the matrix pipe, so in the softmax phase
+    // they would queue behind the other group's MFMAs (measured: a wave of
+    // exp + dot2 runs fully serialised against an MFMA wave on its SIMD,
+    // exp + add overlaps it).
     auto exps = [&]() {
       float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g4 = 0; g4 < 4 * NSUB; ++g4) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 8; ++e) {
           p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g4 >> 1][(g4 & 1) * 8 + e], scale_log2, -m_run));
-        const uint4 pu = pack_bf16x8(p);
-        float ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum[g4 & 3], false);
-        ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, ls, false);
-        ls = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, ls, false);
-        lsum[g4 & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, ls, false);
-        pf[g4] = as_bf16x8(pu);
+          lsum[g4 & 3] += p[e];
+        }
+        pf[g4] = as_bf16x8(pack_bf16x8(p));
+        // keeps the compiler from computing all 32 * NSUB exps before packing
+        // any (their fp32 values would not fit in the register budget)
+        asm volatile("" : "+v"(pf[g4]));
       }
       return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
@@ -745,10 +789,16 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // X(t) for 0 < t < nvt: PV(t-1) then QK(t) as one chain of 32 MFMAs whose
   // LDS operands are read NPRE fragments ahead (a ring of registers), so each
   // MFMA waits only for the oldest read in flight.
-  auto x_full = [&](int t) {
+  // With LOADS (group 0), the NLOAD load slots are spread evenly over the
+  // NX MFMAs: slot floor(i NLOAD / NX) follows MFMA i where that value steps.
+  auto x_full = [&](int t, auto loads) {
+    constexpr bool LOADS = decltype(loads)::value;
     prep_q(t);
     constexpr int NKB = 2 * NSUB;   // 32-key blocks per tile
     constexpr int NPV = 4 * NSUB * NDB, NQK = NKB * NDS, NX = NPV + NQK, NPRE = 6;
+    static_assert(NLOAD <= NX, "at most one load per MFMA");
+    auto is_slot = [](int i) constexpr { return ((i + 1) * NLOAD) / NX > (i * NLOAD) / NX; };
+    auto slot_of = [](int i) constexpr { return (i * NLOAD) / NX; };
     const uint8_t* vb = smem + VB0 + ((t - 1) & 1) * SM::VBYTES + vfrag;
     const uint8_t* kb = smem + KB0 + (t & 1) * SM::KBYTES + kfrag;
     auto frag = [&](int i) -> bf16x8 {
@@ -777,23 +827,35 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         const int ds = (i - NPV) / NKB, kb2 = (i - NPV) % NKB;
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[ds], sacc[kb2], 0, 0, 0);
       }
+      if constexpr (LOADS)
+        if (is_slot(i)) load_slot(t, slot_of(i));
     }
-    // Order: NPRE reads, then (MFMA, read) pairs, then the last MFMAs.
+    // Order: NPRE reads, then (MFMA, read[, load]) groups, then the last MFMAs.
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i + NPRE < NX) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (LOADS && is_slot(i)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
-  issue_k(0);
+  // Group 0 stages K(0) before the first barrier, then K(1) and V(0); from
+  // then on K(t+1) and V(t) inside its X(t) phase.  It waits for its loads at
+  // the end of the following Y phase, whose barrier makes them visible to
+  // both groups before their next use.
+  using kLoads = std::integral_constant<bool, true>;
+  using kNoLoads = std::integral_constant<bool, false>;
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) load_k(0, i);
+  }
   wait_vmem();
   phase_barrier();
   // tile 0 (the first X phase has no PV; the last one, at t = nvt, has no QK)
-  if (nvt > 1) issue_k(1);
-  issue_v(0);
   if (grp == 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < NLOAD; ++s2) load_slot(0, s2);
     prep_q(0);
     do_qk(0);
     phase_barrier();
@@ -801,9 +863,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     wait_vmem();
     phase_barrier();
     for (int t = 1; t < nvt; ++t) {
-      if (t + 1 < nvt) issue_k(t + 1);
-      issue_v(t);
-      x_full(t);
+      x_full(t, kLoads{});
       phase_barrier();
       do_softmax(t);
       wait_vmem();
@@ -816,16 +876,12 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     phase_barrier();
     prep_q(0);
     do_qk(0);
-    wait_vmem();
     phase_barrier();
     for (int t = 1; t < nvt; ++t) {
-      if (t + 1 < nvt) issue_k(t + 1);
-      issue_v(t);
       do_softmax(t - 1);
       pin_p();
       phase_barrier();
-      x_full(t);
-      wait_vmem();
+      x_full(t, kNoLoads{});
       phase_barrier();
     }
     do_softmax(nvt - 1);
