@@ -147,11 +147,12 @@ class ClockSampler:
 
 
 def prefill_kernel_name(c, w, D):
-    """The attention kernel the library launches for bf16 (chunk size s = c - w)."""
+    """The attention kernel the library launches for bf16 (chunk size s = c - w):
+    the DCA map (1) when s is a multiple of 64, else the split map (3)."""
     s = c - w
-    if s % 128 == 0:
-        return f"prefill_bf16_pp_kernel<{D}, 0, 2>"
-    return f"prefill_bf16_pp_kernel<{D}, 0, 1>" if s % 64 == 0 else f"prefill_bf16_kernel<{D}>"
+    if s % 64 == 0:
+        return f"prefill_bf16_pp_kernel<{D}, 0, {2 if s % 128 == 0 else 1}>"
+    return f"prefill_bf16_pp_kernel<{D}, 3, {2 if s >= 256 else 1}>"
 
 
 def cpu_baseline(q, k, v, cfg, seconds):
@@ -190,13 +191,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-128k", action="store_true", help="skip the 131072-token prefill")
     ap.add_argument("--no-7b", action="store_true", help="skip the Llama2-7B-shaped 16k prefill")
+    ap.add_argument("--no-s3096", action="store_true",
+                    help="skip the 32k prefill with chunk size 3096 (not a multiple of the key tiles)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-selfextend", action="store_true", help="skip the SelfExtend 32k prefill")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked 32k prefill and the ragged / paged 100k decodes")
     ap.add_argument("--no-coarse-fine", action="store_true", help="skip the coarse / fine map 32k prefill")
-    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k", "selfextend", "coarsefine"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "prefill128k", "prefill7b", "prefill_s3096", "selfextend",
+                                       "coarsefine"],
+                    default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
@@ -233,7 +238,9 @@ def main():
     run_decode = args.only in (None, "decode")
     run_128k = (args.only == "prefill128k") or (args.only is None and not args.no_128k)
     P7 = inputs.WORKLOADS["llama2_7b_16k"]
-    run_7b = args.only is None and not args.no_7b
+    run_7b = (args.only == "prefill7b") or (args.only is None and not args.no_7b)
+    PS = inputs.WORKLOADS["llama2_70b_32k_s3096"]
+    run_s3096 = (args.only == "prefill_s3096") or (args.only is None and not args.no_s3096)
     SE = inputs.WORKLOADS["selfextend_70b_32k"]
     run_se = (args.only == "selfextend") or (args.only is None and not args.no_selfextend)
     CF = inputs.WORKLOADS["coarse_fine_70b_32k"]
@@ -612,7 +619,46 @@ def main():
                                     "attend_tflops": fl / (att * 1e-3) / 1e12,
                                     "frac": fl / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "steps": n7,
                                     "shape": {k_: P7[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
+        if args.only == "prefill7b":
+            result["value"], result["unit"] = result["prefill_16k_7b"]["tflops"], "TFLOP/s"
+            result["config"] = {"workload": "llama2_7b_16k prefill",
+                                "prefill": {k_: P7[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
         del q7, k7, v7, o7, ws7
+        torch.cuda.empty_cache()
+
+    # ---------------- 32k prefill, chunk size 3096 (reported beside the step) --
+    if run_s3096:
+        log("generating llama2_70b_32k_s3096 inputs")
+        qsh, ksh, vsh = inputs.prefill_inputs(PS["B"], PS["L"], PS["Hq"], PS["Hkv"], PS["D"], "bf16", PS["seed"])
+        qs, ks, vs = qsh.to(dev), ksh.to(dev), vsh.to(dev)
+        del qsh, ksh, vsh
+        os_ = torch.empty_like(qs)
+        wss = torch.empty(dca.prefill_workspace_bytes(PS["B"], PS["L"], PS["Hkv"], PS["D"], PS["c"],
+                                                      torch.bfloat16), dtype=torch.uint8, device=dev)
+        for _ in range(max(5, args.warmup)):   # fresh buffers run slower at first
+            prefill_step(qs, ks, vs, os_, wss, PS, events(3))
+        torch.cuda.synchronize()
+        ns = max(1, args.steps)
+        evs = [events(3) for _ in range(ns)]
+        for i in range(ns):
+            prefill_step(qs, ks, vs, os_, wss, PS, evs[i])
+        torch.cuda.synchronize()
+        prep = sum(e[0].elapsed_time(e[1]) for e in evs) / ns
+        att = sum(e[1].elapsed_time(e[2]) for e in evs) / ns
+        fl = prefill_flops(PS["B"], PS["L"], PS["Hq"], PS["D"])
+        result["prefill_32k_s3096"] = {"ms": prep + att, "prepare_ms": prep, "attend_ms": att,
+                                       "tflops": fl / ((prep + att) * 1e-3) / 1e12,
+                                       "attend_tflops": fl / (att * 1e-3) / 1e12,
+                                       "frac": fl / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "steps": ns,
+                                       "kernel": prefill_kernel_name(PS["c"], PS["w"], PS["D"]),
+                                       "shape": {k_: PS[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
+        if run_prefill:
+            result["prefill_32k_s3096"]["vs_aligned_attend"] = att / result["prefill_32k"]["attend_ms"]
+        if args.only == "prefill_s3096":
+            result["value"], result["unit"] = result["prefill_32k_s3096"]["tflops"], "TFLOP/s"
+            result["config"] = {"workload": "llama2_70b_32k_s3096 prefill",
+                                "prefill": {k_: PS[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
+        del qs, ks, vs, os_, wss
         torch.cuda.empty_cache()
 
     # ---------------- 128k prefill (reported beside the step) ----------------

@@ -76,6 +76,10 @@ enum PosMap : int {
   kMapCoarseFine = 2,  // the DCA guide's own distances: chunk C (held in c and s),
                        // coarse chunk distance scaled by 1/kappa for pairs >= 2
                        // chunks apart, lambda ramp for adjacent chunks
+  kMapDCASplit = 3,    // DCA when the chunk size is not a multiple of the key
+                       // tile or query offsets are not multiples of 32 (kernel
+                       // internal: key tiles cut at chunk boundaries, per-lane
+                       // query variants); chosen by the launcher, never passed in
 };
 // SelfExtend pair classes (the order the kernels visit them in).
 constexpr int kSeGrouped = 0;

@@ -8,14 +8,12 @@
 // softmax over j is merged tile by tile (online max / sum), so no L x L matrix
 // exists.  When the chunk size is a multiple of the tile sizes every (query
 // tile, key tile) pair has one relation, and a tile costs exactly what a plain
-// flash-attention tile costs; otherwise a straddling tile is processed once
-// per relation it contains, with the other relations' pairs masked out.
+// flash-attention tile costs; otherwise the key tiles near the rows' chunks are
+// cut at the chunk boundaries into "virtual tiles" of one relation each.
 //
-// Two bf16 kernels share the tile math below: a two-group "ping-pong" kernel
-// used whenever the chunk size is a multiple of 64 (every (wave, tile) pair
-// has one relation), and a general kernel for any other chunk size.
-//
-// General bf16 kernel (one workgroup = 4 waves = 128 query rows of one head):
+// One bf16 kernel, the two-group "ping-pong" kernel below, serves every map
+// (DCA with any chunk size and query offset, SelfExtend, the guide's coarse /
+// fine map); fp32 inputs take a plain VALU kernel.  Common to both bf16 paths:
 //   * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
 //     wave's 32 rotated queries held in registers.  In the 32x32 output layout
 //     each lane owns one query column, so the row max / sum need a single
@@ -23,16 +21,13 @@
 //   * O^T += V^T * P^T on the same MFMA: A = V^T rows from LDS (pre-transposed
 //     and key-permuted by the prep pass), B = the probabilities straight from
 //     the S^T registers.
-//   * K and V^T tiles of 64 keys are double-buffered in LDS, filled by direct
-//     global->LDS loads (no staging registers); rows padded by 16 bytes make
-//     the MFMA fragment reads bank-conflict free with immediate offsets; one
-//     barrier per tile.
+//   * K and V^T tiles are double-buffered in LDS, filled by direct
+//     global->LDS buffer loads (no staging registers); rows padded by 16 bytes
+//     make the MFMA fragment reads bank-conflict free with immediate offsets.
 //   * The query variant lives in registers and is re-made (rotate raw Q with the
 //     cos/sin table) only when the tile relation changes: inter -> successive
-//     -> intra, at most three times per workgroup on the fast path.
-//   * Online softmax in the log2 domain; rescaling of the accumulator is skipped
-//     while the running max grows by less than 8 (exact: O and l share the
-//     stale max).
+//     -> intra, at most three times per row.
+//   * Online softmax in the log2 domain with a lazy rescale.
 //   * Workgroups are ordered longest causal row first, and, when B*Hkv is a
 //     multiple of 8, mapped so that each XCD (workgroup id mod 8) serves whole
 //     GQA groups and their K/V stay in that XCD's L2.
@@ -45,309 +40,17 @@ namespace dca {
 
 namespace {
 
-constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
-constexpr int BC = kPrefillTileKeys;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNoMax = -1.0e30f;  // running-max sentinel (finite)
 
-// LDS tiles.  Rows are padded by 16 bytes (K: 2D + 16, V^T: 2*64 + 16), which
-// spreads the 16 rows a quarter-wave reads over all 64 banks, and keeps every
-// fragment address of a tile a compile-time offset from one per-lane base.
-// Both tiles are whole multiples of 1 KiB, the unit of a direct-to-LDS load.
-template <int D>
-struct Smem {
-  static constexpr int KROW = D * 2 + 16;
-  static constexpr int VROW = BC * 2 + 16;
-  static constexpr int KBYTES = BC * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int KPIECES = KBYTES / 1024;
-  static constexpr int VPIECES = VBYTES / 1024;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int TOTAL = 2 * STAGE;
-  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole 1 KiB pieces");
-};
-
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ inline bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
-__device__ constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 // s_waitcnt vmcnt(0): this wave's global loads (including the direct-to-LDS
 // ones) have landed.  Encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
-  constexpr int NDS = D / 16;          // MFMA k-steps over the head dim
-  constexpr int NDB = D / 32;          // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<D>::TOTAL];
-
-  // ---- work item ------------------------------------------------------------
-  const int wg = blockIdx.x;
-  int qt_rank, b, hq;
-  const int G = a.Hq / a.Hkv;
-  if (xcd_map) {
-    const int xcd = wg & 7, k = wg >> 3;
-    const int per_rank = (a.B * a.Hkv / 8) * G;
-    qt_rank = k / per_rank;
-    const int rem = k - qt_rank * per_rank;
-    const int slot = (rem / G) * 8 + xcd;
-    b = slot / a.Hkv;
-    hq = (slot - b * a.Hkv) * G + rem % G;
-  } else {
-    const int bh = a.B * a.Hq;
-    qt_rank = wg / bh;
-    const int rem = wg - qt_rank * bh;
-    b = rem / a.Hq;
-    hq = rem - b * a.Hq;
-  }
-  const int qt = nqt - 1 - qt_rank;
-  // This sequence's query rows sit at positions q0 .. q0 + nrows - 1 and see
-  // the keys [0, q0 + nrows).
-  int q0 = 0, nrows = a.L;
-  if (a.per_seq) {
-    q0 = a.seq_q0[b];
-    nrows = a.seq_len[b];
-  }
-  if (qt * BR >= nrows) return;   // whole workgroup, before any barrier
-  const int g = hq / G;
-  const int64_t bg = (int64_t)b * a.Hkv + g;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hh = lane >> 5, ql = lane & 31;
-  const int L = q0 + nrows, s = a.s, c = a.c;
-  const int i0 = q0 + qt * BR;
-  const int qrow = i0 + wave * 32 + ql;
-  const int i_lo = i0 + wave * 32;
-  const int i_hi = min(i_lo + 31, L - 1);
-  const bool wave_live = i_lo < L;
-  const int n_lo = i_lo / s, n_hi = wave_live ? i_hi / s : 0;
-  const int nq = qrow / s, rq = qrow - nq * s;
-  const int last_key = min(i0 + BR - 1, L - 1);
-  const int nkt = last_key / BC + 1;
-
-  const int64_t qoff = (int64_t)b * a.q_rows + (qrow - q0);   // row in q / o
-  const uint16_t* qsrc = (const uint16_t*)a.q + (qoff * a.Hq + hq) * D;
-  const uint16_t* kbase = (const uint16_t*)a.krot + bg * (int64_t)a.Lp * D;
-  const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
-
-  // ---- query variant in registers (B operand of S^T = K Q^T) ------------------
-  // Lane (query ql, half hh) holds dims d = ds*16 + hh*8 + e; the rotate-half
-  // partner d + D/2 is in step ds + NDS/2 of the same lane.
-  bf16x8 qf[NDS];
-  auto load_q = [&](int cls) __attribute__((always_inline)) {
-    const int P = query_pos(cls, rq, s, c);
-    const double2* tb = a.table + (int64_t)P * (D / 2);
-    if (qrow < L) {
-#pragma unroll
-      for (int ds = 0; ds < NDS / 2; ++ds) {
-        const uint4 u1 = *(const uint4*)(qsrc + ds * 16 + hh * 8);
-        const uint4 u2 = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
-        float x1[8], x2[8], y1[8], y2[8];
-        unpack_bf16x8(u1, x1);
-        unpack_bf16x8(u2, x2);
-        // Rotation in fp64, one rounding to bf16 (through fp32).
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double2 t = tb[ds * 16 + hh * 8 + e];
-          y1[e] = (float)((double)x1[e] * t.x - (double)x2[e] * t.y);
-          y2[e] = (float)((double)x2[e] * t.x + (double)x1[e] * t.y);
-        }
-        qf[ds] = as_bf16x8(pack_bf16x8(y1));
-        qf[ds + NDS / 2] = as_bf16x8(pack_bf16x8(y2));
-      }
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) qf[ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
-  };
-
-  // ---- K / V^T staging: direct global -> LDS loads ----------------------------
-  // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS base + 16*l: a wave
-  // fills one 1-KiB piece of the padded tile per instruction.  Each lane's
-  // source offset inside a tile is the same for every tile, so it is computed
-  // once; lanes that land on a row's 16-byte pad fetch that row's first chunk
-  // (a valid address; the pad is never read).  Pieces go round-robin to waves.
-  constexpr int KPW = (Smem<D>::KPIECES + 3) / 4;
-  constexpr int VPW = (Smem<D>::VPIECES + 3) / 4;
-  uint32_t koff[KPW], voff[VPW];
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int byte = (wave + 4 * i) * 1024 + lane * 16;
-    const int row = byte / Smem<D>::KROW, w = byte % Smem<D>::KROW;
-    koff[i] = (uint32_t)(row * D * 2 + (w < D * 2 ? w : 0));
-  }
-#pragma unroll
-  for (int i = 0; i < VPW; ++i) {
-    const int byte = (wave + 4 * i) * 1024 + lane * 16;
-    const int row = byte / Smem<D>::VROW, w = byte % Smem<D>::VROW;
-    voff[i] = (uint32_t)(row * BC * 2 + (w < BC * 2 ? w : 0));
-  }
-  auto issue_tile = [&](int kt, int stage) {
-    const uint8_t* ks = (const uint8_t*)(kbase + (int64_t)kt * BC * D);
-    const uint8_t* vs = (const uint8_t*)(vbase + (int64_t)kt * BC * D);
-    uint8_t* kb = smem + stage * Smem<D>::STAGE;
-    uint8_t* vb = kb + Smem<D>::KBYTES;
-#pragma unroll
-    for (int i = 0; i < KPW; ++i)
-      if (wave + 4 * i < Smem<D>::KPIECES)
-        __builtin_amdgcn_global_load_lds((const void*)(ks + koff[i]),
-                                         (__attribute__((address_space(3))) void*)(kb + (wave + 4 * i) * 1024),
-                                         16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < VPW; ++i)
-      if (wave + 4 * i < Smem<D>::VPIECES)
-        __builtin_amdgcn_global_load_lds((const void*)(vs + voff[i]),
-                                         (__attribute__((address_space(3))) void*)(vb + (wave + 4 * i) * 1024),
-                                         16, 0, 0);
-  };
-  // Per-lane fragment bases: K row (kb*32 + ql), V^T row (db*32 + ql); the
-  // lane's half hh selects the second 16 bytes of each 32-byte k-step.
-  const int kfrag = ql * Smem<D>::KROW + hh * 16;
-  const int vfrag = Smem<D>::KBYTES + ql * Smem<D>::VROW + hh * 16;
-
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-  // Running max (log2 domain).  The finite sentinel keeps rows that have seen
-  // no unmasked key yet NaN-free: their p is exp2(-inf) = 0 and alpha is 1.
-  float m_run = kNoMax, l_run = 0.f;
-  int cur_cls = -1;
-
-  issue_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nkt) issue_tile(kt + 1, stage ^ 1);
-    const int j0 = kt * BC;
-    if (wave_live && j0 <= i_hi) {
-      // Chunk relations present among the unmasked pairs of this wave x tile.
-      const int jmax = min(j0 + BC - 1, i_hi);
-      const int rho_lo = max(n_lo - jmax / s, 0);
-      const int rho_hi = n_hi - j0 / s;
-      const int cls_lo = min(rho_lo, 2), cls_hi = min(rho_hi, 2);
-      const bool straddle = cls_lo != cls_hi;
-      const bool causal = j0 + BC - 1 > i_lo;
-      // A tile whose pairs fall in several relations is processed once per
-      // relation, with the other relations' pairs masked out; the online
-      // softmax merges the pieces like ordinary tiles.
-      for (int cls = cls_lo; cls <= cls_hi; ++cls) {
-        if (cls != cur_cls) {
-          load_q(cls);
-          cur_cls = cls;
-        }
-        // The tile's LDS offset goes through an empty asm so the fragment
-        // reads below are not hoisted out of this (rarely repeated) loop.
-        int toff = stage * Smem<D>::STAGE;
-        asm volatile("" : "+v"(toff));
-        const uint8_t* kb = smem + toff + kfrag;
-        const uint8_t* vb = smem + toff + vfrag;
-        f32x16 sacc[2];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[0][v] = sacc[1][v] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const bf16x8 kf = *(const bf16x8*)(kb + kb2 * 32 * Smem<D>::KROW + ds * 32);
-            sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb2], 0, 0, 0);
-          }
-        }
-        if (causal || straddle) {
-          // Keys this lane keeps: the causal prefix j <= qrow, intersected on a
-          // straddling tile with the key range of relation `cls` for this row
-          // (intra: chunk nq, successive: chunk nq-1, inter: chunks < nq-1).
-          int lo = 0, hi = qrow;
-          if (straddle) {
-            lo = cls == 0 ? nq * s : (cls == 1 ? (nq - 1) * s : 0);
-            hi = min(hi, cls == 0 ? qrow : (cls == 1 ? nq * s - 1 : (nq - 1) * s - 1));
-          }
-          const int jb = j0 + hh * 4;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int j = jb + kb2 * 32 + (v >> 2) * 8 + (v & 3);
-              sacc[kb2][v] = (j >= lo && j <= hi) ? sacc[kb2][v] : -INFINITY;
-            }
-        }
-
-        // ---- online softmax (log2 domain) ----
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb2][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = mx * scale_log2;
-        if (__any(mnew > m_run + kRescaleThreshold)) {
-          const float mn = fmaxf(m_run, mnew);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-          m_run = mn;
-        }
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][u * 8 + e], scale_log2, -m_run));
-            const uint4 pu = pack_bf16x8(p);
-            // Row sum of the bf16-rounded probabilities (the values PV uses).
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.x), kOnes, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.y), kOnes, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.z), kOnes, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pu.w), kOnes, lsum, false);
-            const bf16x8 pf = as_bf16x8(pu);
-            // ---- O^T += V^T P^T for this 16-key group ----
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const bf16x8 vf = *(const bf16x8*)(vb + db * 32 * Smem<D>::VROW + (kb2 * 2 + u) * 32);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
-            }
-          }
-        }
-        l_run += lsum;
-      }
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-
-  // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow < L) {
-    const float inv = 1.f / l_tot;
-    uint16_t* dst = (uint16_t*)a.o + (qoff * a.Hq + hq) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        uint2 wv;
-        wv.x = pack_bf16x2(oacc[db][grp * 4] * inv, oacc[db][grp * 4 + 1] * inv);
-        wv.y = pack_bf16x2(oacc[db][grp * 4 + 2] * inv, oacc[db][grp * 4 + 3] * inv);
-        *(uint2*)(dst + db * 32 + grp * 8 + hh * 4) = wv;
-      }
-    if (hh == 0 && a.lse)
-      a.lse[((int64_t)b * a.Hq + hq) * a.q_rows + (qrow - q0)] = (m_run + log2f(l_tot)) * kLn2;
-  }
-}
-
-// ---- bf16 ping-pong kernel (chunk size a multiple of 64) ------------------------
+// ---- bf16 ping-pong kernel ------------------------------------------------------
 // One workgroup = 8 waves = 256 query rows of one head; key tiles of
 // TK = 64 * NSUB keys (128 when the chunk size allows: half the phase
 // barriers per key, 2-3 % faster than 64).  Waves 0-3 (group 0) and 4-7
@@ -363,9 +66,12 @@ prefill_bf16_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 // load every few MFMAs of its phase 2t, and waited for at the end of phase
 // 2t+1; K and V are each double-buffered.  The softmax row sums add fp32
 // probabilities with plain VALU adds (the bf16 dot2 instructions wait for the
-// matrix pipe and would queue behind the other group's MFMAs).  With s a multiple of TK every 32-row wave block lies in
-// one chunk and every key tile in one chunk, so a (wave, tile) pair has a
-// single relation and no straddle handling is needed.
+// matrix pipe and would queue behind the other group's MFMAs).  With s a
+// multiple of TK (and query offsets multiples of 32) every 32-row wave block
+// lies in one chunk and every key tile in one chunk, so a (wave, tile) pair has
+// a single relation (MAP kMapDCA).  Otherwise (kMapDCASplit) key tiles are cut
+// at the chunk boundaries near the workgroup's rows and each lane picks its
+// own query variant.
 // Maximum of a lane's 32 scores as a tree of max3 (depth 4), so the wave is
 // not held up by a 16-deep dependency chain.
 __device__ inline float max32(const f32x16 (&x)[2]) {
@@ -480,8 +186,11 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const int i0 = q0 + qt * PP_BR;
   const int i_lo = i0 + wave * 32;
   const int qrow = i_lo + ql;
-  const int nq = i_lo / s;                 // the wave's 32 rows share one chunk
-  const int rq = qrow - nq * s;
+  const int nq = i_lo / s;                 // the wave's 32 rows share one chunk (not for kMapDCASplit)
+  // kMapDCASplit (any chunk size and query offset): a wave's 32 rows may span
+  // a chunk boundary, so each lane takes the chunk of its own row.
+  const int nq_l = MAP == kMapDCASplit ? qrow / s : nq;
+  const int rq_l = qrow - nq_l * s;
   const int nkt = min(i0 + PP_BR - 1, L - 1) / TK + 1;
 
   // ---- order in which key tiles are visited ("virtual tiles" t) -------------
@@ -498,8 +207,23 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // whose relation to a tile belongs to the other pass sees it fully masked.
   // (A workgroup's 256 rows can span several chunks, so the key rotation
   // cannot follow one wave's relation: every wave stages part of each tile.)
-  int n_gr = 0, nb_begin = 0, nvt = nkt;
-  if constexpr (MAP == kMapSelfExtend) {
+  // DCA split map: key tiles cut at the chunk boundaries n s with
+  // n >= split_nmin that fall inside a tile.  On the two sides of such a
+  // boundary some row of this workgroup (whose lowest chunk is i0 / s) sees
+  // different relations; older boundaries separate chunks that are both at
+  // least two behind every row (inter on both sides) and are left uncut.  A
+  // virtual tile then holds keys of one relation per row, so each lane can
+  // take its own query variant.
+  int n_gr = 0, nb_begin = 0, nvt = nkt, split_nmin = 1;
+  if constexpr (MAP == kMapDCASplit) {
+    const int key_last = min(i0 + PP_BR - 1, L - 1);
+    split_nmin = max(i0 / s - 1, 1);
+    const int n_hi = key_last / s;
+    if (n_hi >= split_nmin) {
+      const int m = TK / min(s & -s, TK);   // n s is a multiple of TK iff m divides n
+      nvt = nkt + (n_hi - split_nmin + 1) - (n_hi / m - (split_nmin - 1) / m);
+    }
+  } else if constexpr (MAP == kMapSelfExtend) {
     const int W = a.se_window;
     const int i_top = min(i0 + PP_BR - 1, L - 1);
     n_gr = i_top >= W ? (i_top - W) / TK + 1 : 0;
@@ -528,6 +252,40 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     const int rho = nq - (tile_of(t) * TK) / s;
     return t < n_gr ? rho >= 2 : (rho == 0 || rho == 1);
   };
+  // A virtual tile: its index t (LDS buffer parity), its key tile, the keys
+  // [lo, hi] it covers and (split map) the chunk of its first key.  The split
+  // map's tiles are made one after the other from where the previous ended.
+  struct VTile {
+    int t, tile, lo, hi, nk;
+  };
+  auto vt_make = [&](int t) __attribute__((always_inline)) {
+    VTile v;
+    v.t = t;
+    v.tile = tile_of(t);
+    v.lo = v.tile * TK;
+    v.hi = v.lo + TK - 1;
+    v.nk = 0;
+    return v;
+  };
+  auto vt_split = [&](int t, int start) __attribute__((always_inline)) {
+    VTile v;
+    v.t = t;
+    v.tile = start / TK;
+    v.nk = start / s;
+    v.lo = start;
+    const int tile_end = v.tile * TK + TK - 1;
+    const int cut = max(v.nk + 1, split_nmin) * s;   // the next boundary that is cut
+    v.hi = cut <= tile_end ? cut - 1 : tile_end;
+    return v;
+  };
+  auto vt_first = [&]() __attribute__((always_inline)) {
+    if constexpr (MAP == kMapDCASplit) return vt_split(0, 0);
+    else return vt_make(0);
+  };
+  auto vt_next = [&](const VTile& v) __attribute__((always_inline)) {
+    if constexpr (MAP == kMapDCASplit) return vt_split(v.t + 1, v.hi + 1);
+    else return vt_make(v.t + 1);
+  };
 
   const int64_t qoff = (int64_t)b * a.q_rows + (qrow - q0);   // row in q / o
   const uint16_t* qsrc = (const uint16_t*)a.q + (qoff * a.Hq + hq) * D;
@@ -543,7 +301,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     } else {
       const int P = MAP == kMapSelfExtend
                         ? (cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window))
-                        : query_pos(cls, rq, s, c);
+                        : query_pos(cls, rq_l, s, c);
       tb = a.table + (int64_t)P * (D / 2);
     }
     if (qrow < L) {
@@ -625,32 +383,32 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   if constexpr (MAP != kMapDCA)
     krsrc2 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint16_t*)a.krot2 + bg * (int64_t)a.Lp * D), (short)0, head_bytes, kBufferWord3);
-  // K piece slot i of virtual tile tk
-  auto load_k = [&](int tk, int i) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)tile_of(tk) * (uint32_t)(TK * D * 2);
+  // K piece slot i of virtual tile vk
+  auto load_k = [&](const VTile& vk, int i) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)vk.tile * (uint32_t)(TK * D * 2);
     __amdgpu_buffer_rsrc_t rs = krsrc;
     if constexpr (MAP == kMapSelfExtend)
-      if (class_of(tk) == kSeGrouped) rs = krsrc2;
+      if (class_of(vk.t) == kSeGrouped) rs = krsrc2;
     if constexpr (MAP == kMapCoarseFine)
-      if (tk < n_gr) rs = krsrc2;   // the scaled-key pass (same for every wave)
-    uint8_t* dst = smem + KB0 + (tk & 1) * SM::KBYTES + kpiece(i) * 1024;
+      if (vk.t < n_gr) rs = krsrc2;   // the scaled-key pass (same for every wave)
+    uint8_t* dst = smem + KB0 + (vk.t & 1) * SM::KBYTES + kpiece(i) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, (int)koff(i),
                                              (int)soff, 0, 0);
   };
-  // V piece slot i of sub-tile sub of virtual tile t (NSUB consecutive 64-key
+  // V piece slot i of sub-tile sub of virtual tile v (NSUB consecutive 64-key
   // tiles of the HBM layout)
-  auto load_v = [&](int t, int sub, int i) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)(tile_of(t) * NSUB + sub) * (uint32_t)(64 * D * 2);
-    uint8_t* dst = smem + VB0 + (t & 1) * SM::VBYTES + sub * SM::VSUB + vpiece(i) * 1024;
+  auto load_v = [&](const VTile& v, int sub, int i) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)(v.tile * NSUB + sub) * (uint32_t)(64 * D * 2);
+    uint8_t* dst = smem + VB0 + (v.t & 1) * SM::VBYTES + sub * SM::VSUB + vpiece(i) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (__attribute__((address_space(3))) void*)dst, 16, (int)voff(i),
                                              (int)soff, 0, 0);
   };
-  // load slot s of X(t): K(t+1) pieces first, then V(t)
-  auto load_slot = [&](int t, int s) __attribute__((always_inline)) {
+  // load slot s of X(t) (v = t, vn = t + 1): K(t+1) pieces first, then V(t)
+  auto load_slot = [&](const VTile& v, const VTile& vn, int s) __attribute__((always_inline)) {
     if (s < KPW)
-      load_k(t + 1, s);
+      load_k(vn, s);
     else
-      load_v(t, (s - KPW) / VPW, (s - KPW) % VPW);
+      load_v(v, (s - KPW) / VPW, (s - KPW) % VPW);
   };
   const int kfrag = ql * SM::KROW + hh * 16;
   const int vfrag = ql * SM::VROW + hh * 16;
@@ -691,8 +449,9 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sacc[kb2], 0, 0, 0);
       }
   };
-  auto do_softmax = [&](int t) {
-    const int j0 = tile_of(t) * TK;
+  auto do_softmax = [&](const VTile& v) {
+    const int t = v.t;
+    const int j0 = v.tile * TK;
     // Keys this lane keeps: [lo, hi].  DCA: the causal prefix.  SelfExtend:
     // grouped j <= i - W, neighbor i - W < j <= i.  The mask is applied only
     // when the tile is not wholly inside every row's range.
@@ -714,6 +473,11 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         hi = 0;
         need = true;
       }
+    }
+    if constexpr (MAP == kMapDCASplit) {   // the virtual tile's keys only
+      lo = v.lo;
+      hi = min(v.hi, qrow);
+      need = need || v.lo > j0 || v.hi < j0 + TK - 1;
     }
     if (need) {
       const int jb = j0 + hh * 4;
@@ -779,11 +543,22 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // Both groups execute the same number of barriers; each runs its own loop
   // so every iteration is straight-line code.  Tiles past a wave's last row
   // are processed fully masked (p = 0) rather than skipped.
-  auto prep_q = [&](int t) __attribute__((always_inline)) {
-    const int cls = class_of(t);
-    if (cls != cur_cls) {
-      load_q(cls);
-      cur_cls = cls;
+  // The query variant of virtual tile v, re-made when it changes.  Split map:
+  // each lane's own class (rows of one wave can span a chunk boundary); the
+  // wave re-makes its variants when any lane's class changes.
+  auto prep_q = [&](const VTile& v) __attribute__((always_inline)) {
+    if constexpr (MAP == kMapDCASplit) {
+      const int cls = min(max(nq_l - v.nk, 0), 2);
+      if (__any(cls != cur_cls)) {
+        load_q(cls);
+        cur_cls = cls;
+      }
+    } else {
+      const int cls = class_of(v.t);
+      if (cls != cur_cls) {
+        load_q(cls);
+        cur_cls = cls;
+      }
     }
   };
   // X(t) for 0 < t < nvt: PV(t-1) then QK(t) as one chain of 32 MFMAs whose
@@ -791,9 +566,10 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // MFMA waits only for the oldest read in flight.
   // With LOADS (group 0), the NLOAD load slots are spread evenly over the
   // NX MFMAs: slot floor(i NLOAD / NX) follows MFMA i where that value steps.
-  auto x_full = [&](int t, auto loads) {
+  auto x_full = [&](const VTile& v, const VTile& vn, auto loads) {
     constexpr bool LOADS = decltype(loads)::value;
-    prep_q(t);
+    const int t = v.t;
+    prep_q(v);
     constexpr int NKB = 2 * NSUB;   // 32-key blocks per tile
     constexpr int NPV = 4 * NSUB * NDB, NQK = NKB * NDS, NX = NPV + NQK, NPRE = 6;
     static_assert(NLOAD <= NX, "at most one load per MFMA");
@@ -828,7 +604,7 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[ds], sacc[kb2], 0, 0, 0);
       }
       if constexpr (LOADS)
-        if (is_slot(i)) load_slot(t, slot_of(i));
+        if (is_slot(i)) load_slot(v, vn, slot_of(i));
     }
     // Order: NPRE reads, then (MFMA, read[, load]) groups, then the last MFMAs.
 #pragma unroll
@@ -846,26 +622,29 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // both groups before their next use.
   using kLoads = std::integral_constant<bool, true>;
   using kNoLoads = std::integral_constant<bool, false>;
+  VTile vcur = vt_first(), vnxt = vt_next(vcur);
   if (grp == 0) {
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) load_k(0, i);
+    for (int i = 0; i < KPW; ++i) load_k(vcur, i);
   }
   wait_vmem();
   phase_barrier();
   // tile 0 (the first X phase has no PV; the last one, at t = nvt, has no QK)
   if (grp == 0) {
 #pragma unroll
-    for (int s2 = 0; s2 < NLOAD; ++s2) load_slot(0, s2);
-    prep_q(0);
+    for (int s2 = 0; s2 < NLOAD; ++s2) load_slot(vcur, vnxt, s2);
+    prep_q(vcur);
     do_qk(0);
     phase_barrier();
-    do_softmax(0);
+    do_softmax(vcur);
     wait_vmem();
     phase_barrier();
     for (int t = 1; t < nvt; ++t) {
-      x_full(t, kLoads{});
+      vcur = vnxt;
+      vnxt = vt_next(vnxt);
+      x_full(vcur, vnxt, kLoads{});
       phase_barrier();
-      do_softmax(t);
+      do_softmax(vcur);
       wait_vmem();
       phase_barrier();
     }
@@ -874,17 +653,21 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     phase_barrier();
   } else {
     phase_barrier();
-    prep_q(0);
+    prep_q(vcur);
     do_qk(0);
     phase_barrier();
+    VTile vprv = vcur;
     for (int t = 1; t < nvt; ++t) {
-      do_softmax(t - 1);
+      vcur = vnxt;
+      vnxt = vt_next(vnxt);
+      do_softmax(vprv);
       pin_p();
       phase_barrier();
-      x_full(t, kNoLoads{});
+      x_full(vcur, vnxt, kNoLoads{});
       phase_barrier();
+      vprv = vcur;
     }
-    do_softmax(nvt - 1);
+    do_softmax(vprv);
     phase_barrier();
     do_pv(nvt - 1);
     phase_barrier();
@@ -1061,36 +844,31 @@ void launch_pp(const PrefillArgs& a, dim3 grid, int nqt, int xcd_map, float scal
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   const int xcd_map = ((int64_t)a.B * a.Hkv) % 8 == 0 ? 1 : 0;
   const float scale_log2 = a.sm_scale * kLog2e;
-  // DCA takes the two-group kernel when every 32-row wave block and 64-key
-  // tile lies inside one chunk: s a multiple of 64 and query offsets
-  // multiples of 32.  SelfExtend always does.  128-key tiles (half the phase
-  // barriers per key) whenever the chunk size allows them.
-  bool pp = a.s % 64 == 0;
-  if (a.per_seq)
-    for (int i = 0; i < a.B; ++i) pp = pp && a.seq_q0[i] % 32 == 0;
-  if (a.map == kMapCoarseFine && !pp) return hipErrorInvalidValue;   // needs chunk % 64 == 0 (host-checked)
-  if (a.map != kMapDCA || pp) {
-    const bool wide = a.Lp % 128 == 0 && (a.map == kMapSelfExtend || a.s % 128 == 0);
-    const int nqt = (a.q_rows + PP_BR - 1) / PP_BR;
-    const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
-    if (a.map == kMapSelfExtend) {
-      if (wide) launch_pp<kMapSelfExtend, 2>(a, grid, nqt, xcd_map, scale_log2, st);
-      else launch_pp<kMapSelfExtend, 1>(a, grid, nqt, xcd_map, scale_log2, st);
-    } else if (a.map == kMapCoarseFine) {
-      if (wide) launch_pp<kMapCoarseFine, 2>(a, grid, nqt, xcd_map, scale_log2, st);
-      else launch_pp<kMapCoarseFine, 1>(a, grid, nqt, xcd_map, scale_log2, st);
-    } else {
-      if (wide) launch_pp<kMapDCA, 2>(a, grid, nqt, xcd_map, scale_log2, st);
-      else launch_pp<kMapDCA, 1>(a, grid, nqt, xcd_map, scale_log2, st);
-    }
-    return hipGetLastError();
-  }
-  const int nqt = (a.q_rows + BR - 1) / BR;
+  const int nqt = (a.q_rows + PP_BR - 1) / PP_BR;
   const dim3 grid((unsigned)((int64_t)nqt * a.B * a.Hq));
-  if (a.D == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(256), 0, st, a, nqt, xcd_map, scale_log2);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(256), 0, st, a, nqt, xcd_map, scale_log2);
+  // DCA runs the plain map when every 32-row wave block and every 64-key
+  // tile lies inside one chunk (s a multiple of 64, query offsets multiples
+  // of 32), else the split map.  128-key tiles (half the phase barriers per
+  // key) whenever the chunk size allows them; the split map takes them when
+  // chunks are long enough that the extra cut tiles are few.
+  if (a.map == kMapSelfExtend) {
+    launch_pp<kMapSelfExtend, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+  } else if (a.map == kMapCoarseFine) {
+    if (a.s % 64 != 0) return hipErrorInvalidValue;   // needs chunk % 64 == 0 (host-checked)
+    if (a.s % 128 == 0) launch_pp<kMapCoarseFine, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+    else launch_pp<kMapCoarseFine, 1>(a, grid, nqt, xcd_map, scale_log2, st);
+  } else {
+    bool aligned = a.s % 64 == 0;
+    if (a.per_seq)
+      for (int i = 0; i < a.B; ++i) aligned = aligned && a.seq_q0[i] % 32 == 0;
+    if (aligned) {
+      if (a.s % 128 == 0) launch_pp<kMapDCA, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+      else launch_pp<kMapDCA, 1>(a, grid, nqt, xcd_map, scale_log2, st);
+    } else {
+      if (a.s >= 256) launch_pp<kMapDCASplit, 2>(a, grid, nqt, xcd_map, scale_log2, st);
+      else launch_pp<kMapDCASplit, 1>(a, grid, nqt, xcd_map, scale_log2, st);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -78,4 +78,9 @@ WORKLOADS = {
     # trained length 4096, target 32768) on the 70B 32k shape.
     "coarse_fine_70b_32k": dict(kind="coarse_fine", dtype="bf16", B=1, L=32768, Hq=64, Hkv=8, D=128,
                                 chunk=512, train_len=4096, target_len=32768, base=10000.0, seed=6),
+    # The 70B 32k shape with a local window of 1000, so that the chunk size
+    # s = c - w = 3096 is not a multiple of the key tiles (every chunk boundary
+    # falls inside a tile).
+    "llama2_70b_32k_s3096": dict(kind="prefill", dtype="bf16", B=1, L=32768, Hq=64, Hkv=8, D=128,
+                                 c=4096, w=1000, base=10000.0, seed=7),
 }

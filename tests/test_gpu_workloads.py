@@ -200,3 +200,14 @@ def test_decode_100k_discriminating_inputs(monkeypatch):
     # successive pairs as inter changes nothing here; the planted mistake is
     # the successive position left uncapped (s + 1696 = 4768 > c - 1).
     run_decode_workload(qk_scale=2.0, seed_offset=100, mutant=_succ_unsaturated, monkeypatch=monkeypatch)
+
+
+def test_llama2_70b_32k_s3096_sampled_rows():
+    # chunk size 3096: every chunk boundary falls inside a key tile (the split
+    # map of the attention kernel)
+    run_prefill_workload("llama2_70b_32k_s3096", heads=[g * 8 + (g + 3) % 8 for g in range(8)])
+
+
+def test_llama2_70b_32k_s3096_discriminating_inputs(monkeypatch):
+    run_prefill_workload("llama2_70b_32k_s3096", heads=[g * 8 + g % 8 for g in range(8)], qk_scale=2.0,
+                         seed_offset=100, mutant=_succ_as_inter, monkeypatch=monkeypatch)
