@@ -172,12 +172,23 @@ static int prepare_impl(const void* k, const void* v, void* k_rot_out, int64_t B
                         void* ws, const PrefillLayout& p, hipStream_t st) {
   uint8_t* base = (uint8_t*)ws;
   double2* table = (double2*)(base + p.table);
-  hipError_t e = launch_rope_table(table, c, (int)D, rope_base, st);
-  if (e != hipSuccess) return DCA_ERR_HIP;
+  hipError_t e = hipSuccess;
   KvPrepArgs kp = {};
   kp.k = k;
   kp.v = v;
-  kp.table = table;
+  if (dtype == DCA_BF16) {
+    // one launch: keys turned with cos / sin made in the kernel, and the
+    // query cos / sin table written beside them
+    kp.table = nullptr;
+    kp.pos_mode = 2;
+    kp.base = rope_base;
+    kp.table_out = table;
+    kp.table_rows = c;
+  } else {
+    e = launch_rope_table(table, c, (int)D, rope_base, st);
+    if (e != hipSuccess) return DCA_ERR_HIP;
+    kp.table = table;
+  }
   kp.krot = base + p.krot;
   kp.vt = base + p.vt;
   kp.k_rot_out = k_rot_out;

@@ -65,6 +65,13 @@ struct KvPrepArgs {
   double cf_step;
   const double* theta;  // pos_mode 1: theta_k table [D/2]
   PagedKv pg;           // paged k / v (in_rows unused), or bt null
+  // pos_mode 2 (bf16, table null): key j at (j / kdiv) mod kmod with its
+  // cos / sin made in this kernel from base, exactly as launch_rope_table
+  // makes them; the launch also writes that [table_rows][D/2] table to
+  // table_out (for the attention kernel's query rotations).
+  double base;
+  double2* table_out;
+  int table_rows;
 };
 hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st);
 

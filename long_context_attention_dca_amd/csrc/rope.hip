@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
 // loaded before the key work, so their loads are in flight meanwhile, then
 // each head's tile is transposed through LDS and written as whole 16-byte
 // runs of 8 keys (in the key order of vt_perm).
-constexpr int kPrepHeads = 4;
+constexpr int kPrepHeads = 2;
 
 template <int D>
 __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
@@ -281,7 +281,13 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
   const uint16_t* k = (const uint16_t*)a.k;
   const uint16_t* vv = (const uint16_t*)a.v;
   const bool with_v = a.vt != nullptr;
-  const bool rotate = a.table != nullptr || a.pos_mode == 1;
+  const bool rotate = a.table != nullptr || a.pos_mode != 0;
+  // pos_mode 2: theta_k once per workgroup, as the table kernel makes it
+  __shared__ double theta_s[half];
+  if (a.pos_mode == 2) {
+    if (threadIdx.x < half) theta_s[threadIdx.x] = pow(a.base, -2.0 * (double)threadIdx.x / (double)D);
+    __syncthreads();
+  }
 
   // V rows of every head of the group (zero past the valid rows and for
   // unreadable pages).
@@ -322,6 +328,14 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
         const double pos = (double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk);
 #pragma unroll
         for (int e = 0; e < 8; ++e) cs[e] = rope_cs(pos, a.theta[k0 + e]);
+      } else if (a.pos_mode == 2) {
+        const double pos = (double)((j / a.kdiv) % a.kmod);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          double sn, cn;
+          sincos(pos * theta_s[k0 + e], &sn, &cn);
+          cs[e] = make_double2(cn, sn);
+        }
       } else {
         const double2* t = a.table + (int64_t)((j / a.kdiv) % a.kmod) * half + k0;
 #pragma unroll
@@ -356,6 +370,20 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
       }
       *(uint4*)dst = y1;
       *(uint4*)(dst + half) = y2;
+    }
+  }
+
+  // pos_mode 2: this launch also writes the [table_rows][D/2] cos / sin table,
+  // a slice per workgroup.
+  if (a.pos_mode == 2 && a.table_out) {
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+    const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t n = (int64_t)a.table_rows * half;
+    for (int64_t idx = wg * 256 + threadIdx.x; idx < n; idx += nwg * 256) {
+      const int p = (int)(idx / half), kk = (int)(idx - (int64_t)p * half);
+      double sn, cn;
+      sincos((double)p * theta_s[kk], &sn, &cn);
+      a.table_out[idx] = make_double2(cn, sn);
     }
   }
 
