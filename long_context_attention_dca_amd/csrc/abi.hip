@@ -185,7 +185,7 @@ static int prepare_impl(const void* k, const void* v, void* k_rot_out, int64_t B
     kp.table_out = table;
     kp.table_rows = c;
   } else {
-    e = launch_rope_table(table, c, (int)D, rope_base, st);
+    e = launch_rope_table(table, c, (int)D, rope_base, false, st);   // the key pass reads rows
     if (e != hipSuccess) return DCA_ERR_HIP;
     kp.table = table;
   }
@@ -218,6 +218,9 @@ static int attend_impl(const void* q, void* o, float* lse, int64_t B, int64_t L,
   a.krot = base + p.krot;
   a.vt = base + p.vt;
   a.table = (const double2*)(base + p.table);
+  // bf16: the prepare launch wrote it frequency-major; fp32: row-major
+  a.tab_ps = dtype == DCA_BF16 ? 1 : D / 2;
+  a.tab_ks = dtype == DCA_BF16 ? c : 1;
   a.o = o;
   a.lse = lse;
   a.B = (int)B;
@@ -311,7 +314,7 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   hipStream_t st = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
   double2* table = (double2*)(base + p.table);
-  if (launch_rope_table(table, (int)p.npos, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  if (launch_rope_table(table, (int)p.npos, (int)D, rope_base, false, st) != hipSuccess) return DCA_ERR_HIP;
   // neighbor keys at j (with the V layout), grouped keys at floor(j / G)
   const int unbounded = 1 << 30;
   KvPrepArgs kp = {};
@@ -342,6 +345,8 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   a.krot2 = base + p.krot2;
   a.vt = base + p.vt;
   a.table = table;
+  a.tab_ps = D / 2;   // row-major: the key passes read it too
+  a.tab_ks = 1;
   a.o = o;
   a.lse = lse;
   a.B = (int)B;
@@ -444,6 +449,8 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
   a.krot2 = base + p.krot2;
   a.vt = dtype == DCA_BF16 ? (const void*)(base + p.vt) : v;   // fp32 reads V as given
   a.table = qtab;
+  a.tab_ps = 1;   // frequency-major over the 3 L query positions
+  a.tab_ks = 3 * L;
   a.o = o;
   a.lse = lse;
   a.B = (int)B;
@@ -544,7 +551,7 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
   hipStream_t st = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
   double2* table = (double2*)(base + p.table);
-  if (launch_rope_table(table, c, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  if (launch_rope_table(table, c, (int)D, rope_base, true, st) != hipSuccess) return DCA_ERR_HIP;
   const int64_t es = elem_size(dtype);
   const int64_t kv_seq = cache_len * Hkv * D * es;    // bytes of one sequence's cache
   const int64_t ws_seq = Hkv * p.Lp * D * es;         // bytes of one sequence's tiles
@@ -582,6 +589,8 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
     // bf16 reads the V tiles; fp32 reads the cache's values directly
     a.vt = dtype == DCA_BF16 ? kp.vt : kp.v;
     a.table = table;
+    a.tab_ps = 1;   // frequency-major
+    a.tab_ks = c;
     a.o = (uint8_t*)o + b0 * Lq * Hq * D * es;
     a.lse = lse ? lse + b0 * Hq * Lq : nullptr;
     a.B = nb;

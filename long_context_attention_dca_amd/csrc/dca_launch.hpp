@@ -16,11 +16,12 @@ constexpr int kMaxSeqGroup = 64;
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // RoPE cos/sin table [npos][D/2] of double2 (cos, sin), all in fp64.
-hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipStream_t st);
+// kmajor: the frequency-major layout [D/2][npos] instead.
+hipError_t launch_rope_table(double2* table, int npos, int D, double base, bool kmajor, hipStream_t st);
 // theta_k = base^(-2k/D) for k < D/2, fp64 (for real-valued positions).
 hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st);
 // Coarse / fine map: (cos, sin) of the three query positions of rows 0 .. L-1,
-// [3][L][D/2] double2, from theta (chunk C, 1 / kappa = inv_kappa).
+// frequency-major [D/2][3][L] double2, from theta (chunk C, 1 / kappa = inv_kappa).
 hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
                                  hipStream_t st);
 
@@ -67,8 +68,9 @@ struct KvPrepArgs {
   PagedKv pg;           // paged k / v (in_rows unused), or bt null
   // pos_mode 2 (bf16, table null): key j at (j / kdiv) mod kmod with its
   // cos / sin made in this kernel from base, exactly as launch_rope_table
-  // makes them; the launch also writes that [table_rows][D/2] table to
-  // table_out (for the attention kernel's query rotations).
+  // makes them; the launch also writes that table, frequency-major
+  // ([D/2][table_rows]), to table_out (for the attention kernel's query
+  // rotations).
   double base;
   double2* table_out;
   int table_rows;
@@ -97,8 +99,14 @@ struct PrefillArgs {
   const void* krot;    // [B, Hkv, Lp, D] rotated keys (DCA: at j mod s; SelfExtend: at j)
   const void* krot2;   // SelfExtend only: keys at floor(j / G); null for DCA
   const void* vt;      // bf16: [B, Hkv, Lp/64, D, 64]; fp32: raw v [B, L, Hkv, D]
-  const double2* table; // [npos, D/2] (cos, sin) in fp64; kMapCoarseFine: [3][L][D/2],
-                        // the intra / successive / inter query positions of every row
+  const double2* table; // (cos, sin) in fp64 of npos positions x D/2 frequencies; kMapCoarseFine:
+                        // 3 L positions, the intra / successive / inter query positions of row i
+                        // at cls * L + i
+  // Element (position P, frequency k) is table[P * tab_ps + k * tab_ks]: row-major
+  // (tab_ps = D/2, tab_ks = 1) or frequency-major (tab_ps = 1, tab_ks = npos).  The
+  // frequency-major form lets a wave's 32 consecutive query positions read one
+  // frequency's (cos, sin) as contiguous 512 bytes instead of 32 separate rows.
+  int64_t tab_ps, tab_ks;
   void* o;             // [B, L, Hq, D]
   float* lse;          // [B, Hq, L] or null
   int B, L, Lp, Hq, Hkv, D, c, w, s;

@@ -12,22 +12,32 @@
 
 namespace dca {
 
-// ---- cos/sin table [npos][D/2] (fp64) ----------------------------------------------
-__global__ void rope_table_kernel(double2* __restrict__ table, int npos, int half, int D, double base) {
+// ---- cos/sin table (fp64), [npos][D/2] or frequency-major [D/2][npos] -------------------
+// Thread idx covers entry idx of the layout it writes, so the stores are
+// contiguous either way.
+__global__ void rope_table_kernel(double2* __restrict__ table, int npos, int half, int D, double base,
+                                  int kmajor) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= npos * half) return;
-  const int p = idx / half, k = idx - p * half;
+  int p, k;
+  if (kmajor) {
+    k = idx / npos;
+    p = idx - k * npos;
+  } else {
+    p = idx / half;
+    k = idx - p * half;
+  }
   const double theta = pow(base, -2.0 * (double)k / (double)D);
   double sn, cs;
   sincos((double)p * theta, &sn, &cs);
   table[idx] = make_double2(cs, sn);
 }
 
-hipError_t launch_rope_table(double2* table, int npos, int D, double base, hipStream_t st) {
+hipError_t launch_rope_table(double2* table, int npos, int D, double base, bool kmajor, hipStream_t st) {
   const int half = D / 2;
   const int n = npos * half;
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, npos, half, D,
-                     base);
+                     base, kmajor ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -41,15 +51,18 @@ hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st) 
   return hipGetLastError();
 }
 
-__global__ void cf_query_table_kernel(double2* __restrict__ tab, int L, int half, int C, double inv_kappa,
+// Frequency-major: entry (cls * L + i, k) at k * 3L + cls * L + i.
+__global__ void cf_query_table_kernel(double2* __restrict__ tab, int L, int C, double inv_kappa,
                                       const double* __restrict__ theta) {
-  const int i = blockIdx.x, cls = blockIdx.y, k = threadIdx.x;
-  if (k < half) tab[((int64_t)cls * L + i) * half + k] = rope_cs(cf_query_pos(cls, i, C, inv_kappa), theta[k]);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x, cls = blockIdx.y, k = blockIdx.z;
+  if (i < L)
+    tab[(int64_t)k * 3 * L + (int64_t)cls * L + i] = rope_cs(cf_query_pos(cls, i, C, inv_kappa), theta[k]);
 }
 
 hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
                                  hipStream_t st) {
-  hipLaunchKernelGGL(cf_query_table_kernel, dim3(L, 3), dim3(64), 0, st, tab, L, D / 2, C, inv_kappa, theta);
+  hipLaunchKernelGGL(cf_query_table_kernel, dim3((L + 255) / 256, 3, D / 2), dim3(256), 0, st, tab, L, C,
+                     inv_kappa, theta);
   return hipGetLastError();
 }
 
@@ -373,14 +386,15 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
     }
   }
 
-  // pos_mode 2: this launch also writes the [table_rows][D/2] cos / sin table,
-  // a slice per workgroup.
+  // pos_mode 2: this launch also writes the cos / sin table of positions
+  // 0 .. table_rows - 1, frequency-major ([D/2][table_rows]), a slice per
+  // workgroup.
   if (a.pos_mode == 2 && a.table_out) {
     const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
     const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     const int64_t n = (int64_t)a.table_rows * half;
     for (int64_t idx = wg * 256 + threadIdx.x; idx < n; idx += nwg * 256) {
-      const int p = (int)(idx / half), kk = (int)(idx - (int64_t)p * half);
+      const int kk = (int)(idx / a.table_rows), p = (int)(idx - (int64_t)kk * a.table_rows);
       double sn, cn;
       sincos((double)p * theta_s[kk], &sn, &cn);
       a.table_out[idx] = make_double2(cn, sn);
