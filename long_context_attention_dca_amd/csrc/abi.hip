@@ -178,11 +178,11 @@ static int prepare_impl(const void* k, const void* v, void* k_rot_out, int64_t B
   kp.v = v;
   if (dtype == DCA_BF16) {
     // one launch: keys turned with cos / sin made in the kernel, and the
-    // query cos / sin table written beside them
+    // query cos / sin table (fp32) written beside them
     kp.table = nullptr;
     kp.pos_mode = 2;
     kp.base = rope_base;
-    kp.table_out = table;
+    kp.table_out = (float2*)table;
     kp.table_rows = c;
   } else {
     e = launch_rope_table(table, c, (int)D, rope_base, false, st);   // the key pass reads rows
@@ -217,10 +217,16 @@ static int attend_impl(const void* q, void* o, float* lse, int64_t B, int64_t L,
   a.q = q;
   a.krot = base + p.krot;
   a.vt = base + p.vt;
-  a.table = (const double2*)(base + p.table);
-  // bf16: the prepare launch wrote it frequency-major; fp32: row-major
-  a.tab_ps = dtype == DCA_BF16 ? 1 : D / 2;
-  a.tab_ks = dtype == DCA_BF16 ? c : 1;
+  // bf16: the prepare launch wrote it in fp32, frequency-major; fp32: fp64, row-major
+  if (dtype == DCA_BF16) {
+    a.ftable = (const float2*)(base + p.table);
+    a.tab_ps = 1;
+    a.tab_ks = c;
+  } else {
+    a.table = (const double2*)(base + p.table);
+    a.tab_ps = D / 2;
+    a.tab_ks = 1;
+  }
   a.o = o;
   a.lse = lse;
   a.B = (int)B;
@@ -550,8 +556,11 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
   if (!ws || ws_bytes < p.total || !aligned(ws, 256)) return DCA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
+  // query cos / sin, frequency-major: fp32 for the bf16 kernel, fp64 for the fp32 one
   double2* table = (double2*)(base + p.table);
-  if (launch_rope_table(table, c, (int)D, rope_base, true, st) != hipSuccess) return DCA_ERR_HIP;
+  if ((dtype == DCA_BF16 ? launch_rope_table_f32((float2*)table, c, (int)D, rope_base, st)
+                         : launch_rope_table(table, c, (int)D, rope_base, true, st)) != hipSuccess)
+    return DCA_ERR_HIP;
   const int64_t es = elem_size(dtype);
   const int64_t kv_seq = cache_len * Hkv * D * es;    // bytes of one sequence's cache
   const int64_t ws_seq = Hkv * p.Lp * D * es;         // bytes of one sequence's tiles
@@ -588,7 +597,10 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
     a.krot2 = nullptr;
     // bf16 reads the V tiles; fp32 reads the cache's values directly
     a.vt = dtype == DCA_BF16 ? kp.vt : kp.v;
-    a.table = table;
+    if (dtype == DCA_BF16)
+      a.ftable = (const float2*)table;
+    else
+      a.table = table;
     a.tab_ps = 1;   // frequency-major
     a.tab_ks = c;
     a.o = (uint8_t*)o + b0 * Lq * Hq * D * es;

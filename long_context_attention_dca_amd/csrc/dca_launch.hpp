@@ -18,6 +18,9 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // RoPE cos/sin table [npos][D/2] of double2 (cos, sin), all in fp64.
 // kmajor: the frequency-major layout [D/2][npos] instead.
 hipError_t launch_rope_table(double2* table, int npos, int D, double base, bool kmajor, hipStream_t st);
+// The same angles rounded to fp32, frequency-major [D/2][npos] float2 (the bf16
+// prefill kernel's DCA query rotations).
+hipError_t launch_rope_table_f32(float2* table, int npos, int D, double base, hipStream_t st);
 // theta_k = base^(-2k/D) for k < D/2, fp64 (for real-valued positions).
 hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st);
 // Coarse / fine map: (cos, sin) of the three query positions of rows 0 .. L-1,
@@ -68,11 +71,11 @@ struct KvPrepArgs {
   PagedKv pg;           // paged k / v (in_rows unused), or bt null
   // pos_mode 2 (bf16, table null): key j at (j / kdiv) mod kmod with its
   // cos / sin made in this kernel from base, exactly as launch_rope_table
-  // makes them; the launch also writes that table, frequency-major
-  // ([D/2][table_rows]), to table_out (for the attention kernel's query
-  // rotations).
+  // makes them; the launch also writes that table rounded to fp32,
+  // frequency-major ([D/2][table_rows]), to table_out (for the attention
+  // kernel's query rotations).
   double base;
-  double2* table_out;
+  float2* table_out;
   int table_rows;
 };
 hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st);
@@ -107,6 +110,9 @@ struct PrefillArgs {
   // frequency-major form lets a wave's 32 consecutive query positions read one
   // frequency's (cos, sin) as contiguous 512 bytes instead of 32 separate rows.
   int64_t tab_ps, tab_ks;
+  // bf16 kernel, DCA maps: the table's angles rounded to fp32 (float2), with
+  // the same strides; read instead of table.
+  const float2* ftable;
   void* o;             // [B, L, Hq, D]
   float* lse;          // [B, Hq, L] or null
   int B, L, Lp, Hq, Hkv, D, c, w, s;

@@ -294,6 +294,45 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
 
   bf16x8 qf[NDS];
   auto load_q = [&](int cls) __attribute__((always_inline)) {
+    if constexpr (MAP == kMapDCA || MAP == kMapDCASplit) {
+      // fp32 angles (frequency-major) and fp32 arithmetic: a lane's 32 pairs
+      // and its raw query fit in registers at once, so all loads are in
+      // flight together, and the rotation costs 4 fp32 operations per pair
+      // (fp64 needs about 10 at the same per-instruction rate, and this runs
+      // beside the other group's softmax on the same SIMD).  Rounding the
+      // angles and the rotation to fp32 moves a query by a few 2^-24,
+      // far below its bf16 rounding.
+      if (qrow < L) {
+        const float2* ft = a.ftable + (int64_t)query_pos(cls, rq_l, s, c) * a.tab_ps + (int64_t)(hh * 8) * a.tab_ks;
+        uint4 u[NDS];
+        float2 tv[NDS / 2][8];
+#pragma unroll
+        for (int ds = 0; ds < NDS / 2; ++ds) {
+          u[ds] = *(const uint4*)(qsrc + ds * 16 + hh * 8);
+          u[ds + NDS / 2] = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tv[ds][e] = ft[(int64_t)(ds * 16 + e) * a.tab_ks];
+        }
+#pragma unroll
+        for (int ds = 0; ds < NDS / 2; ++ds) {
+          float x1[8], x2[8], y1[8], y2[8];
+          unpack_bf16x8(u[ds], x1);
+          unpack_bf16x8(u[ds + NDS / 2], x2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float cs = tv[ds][e].x, sn = tv[ds][e].y;
+            y1[e] = fmaf(x1[e], cs, -(x2[e] * sn));
+            y2[e] = fmaf(x2[e], cs, x1[e] * sn);
+          }
+          qf[ds] = as_bf16x8(pack_bf16x8(y1));
+          qf[ds + NDS / 2] = as_bf16x8(pack_bf16x8(y2));
+        }
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) qf[ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      }
+      return;
+    }
     // this row's (cos, sin) at its query position, read only for rows < L;
     // frequency k at tb[k * tab_ks].  Frequency-major tables (tab_ps = 1) let
     // the 32 consecutive positions of a wave read each frequency as 512

@@ -41,6 +41,22 @@ hipError_t launch_rope_table(double2* table, int npos, int D, double base, bool 
   return hipGetLastError();
 }
 
+__global__ void rope_table_f32_kernel(float2* __restrict__ table, int npos, int D, double base) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= npos * (D / 2)) return;
+  const int k = idx / npos, p = idx - k * npos;
+  const double theta = pow(base, -2.0 * (double)k / (double)D);
+  double sn, cs;
+  sincos((double)p * theta, &sn, &cs);
+  table[idx] = make_float2((float)cs, (float)sn);
+}
+
+hipError_t launch_rope_table_f32(float2* table, int npos, int D, double base, hipStream_t st) {
+  const int n = npos * (D / 2);
+  hipLaunchKernelGGL(rope_table_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, npos, D, base);
+  return hipGetLastError();
+}
+
 __global__ void rope_theta_kernel(double* __restrict__ theta, int half, int D, double base) {
   const int k = threadIdx.x;
   if (k < half) theta[k] = pow(base, -2.0 * (double)k / (double)D);
@@ -387,8 +403,8 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
   }
 
   // pos_mode 2: this launch also writes the cos / sin table of positions
-  // 0 .. table_rows - 1, frequency-major ([D/2][table_rows]), a slice per
-  // workgroup.
+  // 0 .. table_rows - 1 in fp32, frequency-major ([D/2][table_rows]), a slice
+  // per workgroup.
   if (a.pos_mode == 2 && a.table_out) {
     const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
     const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
@@ -397,7 +413,7 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
       const int kk = (int)(idx / a.table_rows), p = (int)(idx - (int64_t)kk * a.table_rows);
       double sn, cn;
       sincos((double)p * theta_s[kk], &sn, &cn);
-      a.table_out[idx] = make_double2(cn, sn);
+      a.table_out[idx] = make_float2((float)cn, (float)sn);
     }
   }
 
