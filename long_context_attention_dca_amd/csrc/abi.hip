@@ -320,13 +320,22 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   hipStream_t st = (hipStream_t)stream;
   uint8_t* base = (uint8_t*)ws;
   double2* table = (double2*)(base + p.table);
-  if (launch_rope_table(table, (int)p.npos, (int)D, rope_base, false, st) != hipSuccess) return DCA_ERR_HIP;
   // neighbor keys at j (with the V layout), grouped keys at floor(j / G)
   const int unbounded = 1 << 30;
   KvPrepArgs kp = {};
   kp.k = k;
   kp.v = v;
-  kp.table = table;
+  if (dtype == DCA_BF16) {
+    // keys turned with cos / sin made in the kernel; the first launch also
+    // writes the query cos / sin table (fp32, frequency-major)
+    kp.pos_mode = 2;
+    kp.base = rope_base;
+    kp.table_out = (float2*)table;
+    kp.table_rows = (int)p.npos;
+  } else {
+    if (launch_rope_table(table, (int)p.npos, (int)D, rope_base, false, st) != hipSuccess) return DCA_ERR_HIP;
+    kp.table = table;
+  }
   kp.krot = base + p.krot;
   kp.vt = base + p.vt;
   kp.B = (int)B;
@@ -341,6 +350,7 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   kp.krot = base + p.krot2;
   kp.vt = nullptr;
   kp.kdiv = group;
+  kp.table_out = nullptr;
   if (launch_kv_prep(kp, dtype, st) != hipSuccess) return DCA_ERR_HIP;
   if (dtype == DCA_F32 &&
       hipMemcpyAsync(base + p.vt, v, (size_t)(B * L * Hkv * D * 4), hipMemcpyDeviceToDevice, st) != hipSuccess)
@@ -350,9 +360,15 @@ int dca_selfextend_prefill(const void* q, const void* k, const void* v, void* o,
   a.krot = base + p.krot;
   a.krot2 = base + p.krot2;
   a.vt = base + p.vt;
-  a.table = table;
-  a.tab_ps = D / 2;   // row-major: the key passes read it too
-  a.tab_ks = 1;
+  if (dtype == DCA_BF16) {
+    a.ftable = (const float2*)table;
+    a.tab_ps = 1;   // frequency-major
+    a.tab_ks = p.npos;
+  } else {
+    a.table = table;
+    a.tab_ps = D / 2;   // row-major: the key passes read it too
+    a.tab_ks = 1;
+  }
   a.o = o;
   a.lse = lse;
   a.B = (int)B;
@@ -423,8 +439,11 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
   const double inv_kappa = (double)train_len / (double)target_len;
   double* theta = (double*)base;
   if (launch_rope_theta(theta, (int)D, rope_base, st) != hipSuccess) return DCA_ERR_HIP;
+  // query cos / sin, frequency-major: fp32 for the bf16 kernel, fp64 for the fp32 one
   double2* qtab = (double2*)(base + p.qtab);
-  if (launch_cf_query_table(qtab, (int)L, (int)D, chunk, inv_kappa, theta, st) != hipSuccess) return DCA_ERR_HIP;
+  if ((dtype == DCA_BF16 ? launch_cf_query_table_f32((float2*)qtab, (int)L, (int)D, chunk, inv_kappa, theta, st)
+                         : launch_cf_query_table(qtab, (int)L, (int)D, chunk, inv_kappa, theta, st)) != hipSuccess)
+    return DCA_ERR_HIP;
   // keys at plain positions (with the V layout), then at coarse-scaled positions
   KvPrepArgs kp = {};
   kp.k = k;
@@ -454,7 +473,10 @@ int dca_coarse_fine_prefill(const void* q, const void* k, const void* v, void* o
   a.krot = base + p.krot;
   a.krot2 = base + p.krot2;
   a.vt = dtype == DCA_BF16 ? (const void*)(base + p.vt) : v;   // fp32 reads V as given
-  a.table = qtab;
+  if (dtype == DCA_BF16)
+    a.ftable = (const float2*)qtab;
+  else
+    a.table = qtab;
   a.tab_ps = 1;   // frequency-major over the 3 L query positions
   a.tab_ks = 3 * L;
   a.o = o;

@@ -27,6 +27,9 @@ hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st);
 // frequency-major [D/2][3][L] double2, from theta (chunk C, 1 / kappa = inv_kappa).
 hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
                                  hipStream_t st);
+// The same, rounded to fp32 (the bf16 prefill kernel).
+hipError_t launch_cf_query_table_f32(float2* tab, int L, int D, int C, double inv_kappa, const double* theta,
+                                     hipStream_t st);
 
 // dca_rope_remap kernel (dtype 0 = fp32, 1 = bf16).  map kRemapCoarseScaled
 // (internal): the coarse / fine map's scaled key position, floor(p / c) *
@@ -102,7 +105,7 @@ struct PrefillArgs {
   const void* krot;    // [B, Hkv, Lp, D] rotated keys (DCA: at j mod s; SelfExtend: at j)
   const void* krot2;   // SelfExtend only: keys at floor(j / G); null for DCA
   const void* vt;      // bf16: [B, Hkv, Lp/64, D, 64]; fp32: raw v [B, L, Hkv, D]
-  const double2* table; // (cos, sin) in fp64 of npos positions x D/2 frequencies; kMapCoarseFine:
+  const double2* table; // fp32 kernel: (cos, sin) in fp64 of npos positions x D/2 frequencies; kMapCoarseFine:
                         // 3 L positions, the intra / successive / inter query positions of row i
                         // at cls * L + i
   // Element (position P, frequency k) is table[P * tab_ps + k * tab_ks]: row-major
@@ -110,8 +113,8 @@ struct PrefillArgs {
   // frequency-major form lets a wave's 32 consecutive query positions read one
   // frequency's (cos, sin) as contiguous 512 bytes instead of 32 separate rows.
   int64_t tab_ps, tab_ks;
-  // bf16 kernel, DCA maps: the table's angles rounded to fp32 (float2), with
-  // the same strides; read instead of table.
+  // The bf16 kernel reads the angles rounded to fp32 (float2) here, with the
+  // same strides; table is then unused.
   const float2* ftable;
   void* o;             // [B, L, Hq, D]
   float* lse;          // [B, Hq, L] or null

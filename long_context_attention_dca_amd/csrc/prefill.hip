@@ -293,74 +293,45 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   const uint16_t* vbase = (const uint16_t*)a.vt + bg * (int64_t)a.Lp * D;
 
   bf16x8 qf[NDS];
+  // The query variant of class cls: the raw query turned by the (cos, sin)
+  // of its query position, read from the fp32 frequency-major table (element
+  // (P, k) at P * tab_ps + k * tab_ks): the 32 consecutive positions of a
+  // wave read each frequency as 256 contiguous bytes.  A lane's 32 pairs and
+  // its raw query fit in registers at once, so all its loads are in flight
+  // together, and the rotation costs 4 fp32 operations per pair (fp64 needs
+  // about 10 at the same per-instruction rate, beside the other group's
+  // softmax on the same SIMD).  Rounding the angles and the rotation to fp32
+  // moves a query by a few 2^-24, far below its bf16 rounding.  Rows past the
+  // end get zero queries.
   auto load_q = [&](int cls) __attribute__((always_inline)) {
-    if constexpr (MAP == kMapDCA || MAP == kMapDCASplit) {
-      // fp32 angles (frequency-major) and fp32 arithmetic: a lane's 32 pairs
-      // and its raw query fit in registers at once, so all loads are in
-      // flight together, and the rotation costs 4 fp32 operations per pair
-      // (fp64 needs about 10 at the same per-instruction rate, and this runs
-      // beside the other group's softmax on the same SIMD).  Rounding the
-      // angles and the rotation to fp32 moves a query by a few 2^-24,
-      // far below its bf16 rounding.
-      if (qrow < L) {
-        const float2* ft = a.ftable + (int64_t)query_pos(cls, rq_l, s, c) * a.tab_ps + (int64_t)(hh * 8) * a.tab_ks;
-        uint4 u[NDS];
-        float2 tv[NDS / 2][8];
-#pragma unroll
-        for (int ds = 0; ds < NDS / 2; ++ds) {
-          u[ds] = *(const uint4*)(qsrc + ds * 16 + hh * 8);
-          u[ds + NDS / 2] = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) tv[ds][e] = ft[(int64_t)(ds * 16 + e) * a.tab_ks];
-        }
-#pragma unroll
-        for (int ds = 0; ds < NDS / 2; ++ds) {
-          float x1[8], x2[8], y1[8], y2[8];
-          unpack_bf16x8(u[ds], x1);
-          unpack_bf16x8(u[ds + NDS / 2], x2);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float cs = tv[ds][e].x, sn = tv[ds][e].y;
-            y1[e] = fmaf(x1[e], cs, -(x2[e] * sn));
-            y2[e] = fmaf(x2[e], cs, x1[e] * sn);
-          }
-          qf[ds] = as_bf16x8(pack_bf16x8(y1));
-          qf[ds + NDS / 2] = as_bf16x8(pack_bf16x8(y2));
-        }
-      } else {
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) qf[ds] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      }
-      return;
-    }
-    // this row's (cos, sin) at its query position, read only for rows < L;
-    // frequency k at tb[k * tab_ks].  Frequency-major tables (tab_ps = 1) let
-    // the 32 consecutive positions of a wave read each frequency as 512
-    // contiguous bytes: re-making a variant then costs a workgroup about 40 %
-    // less time than with one 1 KiB table row per lane.
-    const double2* tb;
-    if constexpr (MAP == kMapCoarseFine) {   // real positions: one table row per (variant, row)
-      tb = a.table + ((int64_t)cls * a.L + qrow) * a.tab_ps;
-    } else {
-      const int P = MAP == kMapSelfExtend
-                        ? (cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window))
-                        : query_pos(cls, rq_l, s, c);
-      tb = a.table + (int64_t)P * a.tab_ps;
-    }
     if (qrow < L) {
-      tb += (int64_t)(hh * 8) * a.tab_ks;
+      int64_t P;
+      if constexpr (MAP == kMapCoarseFine)   // real positions: one table entry per (variant, row)
+        P = (int64_t)cls * a.L + qrow;
+      else if constexpr (MAP == kMapSelfExtend)
+        P = cls == kSeNeighbor ? qrow : se_query_pos_grouped(qrow, a.se_group, a.se_window);
+      else
+        P = query_pos(cls, rq_l, s, c);
+      const float2* ft = a.ftable + P * a.tab_ps + (int64_t)(hh * 8) * a.tab_ks;
+      uint4 u[NDS];
+      float2 tv[NDS / 2][8];
 #pragma unroll
       for (int ds = 0; ds < NDS / 2; ++ds) {
-        const uint4 u1 = *(const uint4*)(qsrc + ds * 16 + hh * 8);
-        const uint4 u2 = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
+        u[ds] = *(const uint4*)(qsrc + ds * 16 + hh * 8);
+        u[ds + NDS / 2] = *(const uint4*)(qsrc + (ds + NDS / 2) * 16 + hh * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tv[ds][e] = ft[(int64_t)(ds * 16 + e) * a.tab_ks];
+      }
+#pragma unroll
+      for (int ds = 0; ds < NDS / 2; ++ds) {
         float x1[8], x2[8], y1[8], y2[8];
-        unpack_bf16x8(u1, x1);
-        unpack_bf16x8(u2, x2);
+        unpack_bf16x8(u[ds], x1);
+        unpack_bf16x8(u[ds + NDS / 2], x2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const double2 t = tb[(int64_t)(ds * 16 + e) * a.tab_ks];
-          y1[e] = (float)((double)x1[e] * t.x - (double)x2[e] * t.y);
-          y2[e] = (float)((double)x2[e] * t.x + (double)x1[e] * t.y);
+          const float cs = tv[ds][e].x, sn = tv[ds][e].y;
+          y1[e] = fmaf(x1[e], cs, -(x2[e] * sn));
+          y2[e] = fmaf(x2[e], cs, x1[e] * sn);
         }
         qf[ds] = as_bf16x8(pack_bf16x8(y1));
         qf[ds + NDS / 2] = as_bf16x8(pack_bf16x8(y2));

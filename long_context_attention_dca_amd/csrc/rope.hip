@@ -67,19 +67,35 @@ hipError_t launch_rope_theta(double* theta, int D, double base, hipStream_t st) 
   return hipGetLastError();
 }
 
-// Frequency-major: entry (cls * L + i, k) at k * 3L + cls * L + i.
-__global__ void cf_query_table_kernel(double2* __restrict__ tab, int L, int C, double inv_kappa,
+// Frequency-major: entry (cls * L + i, k) at k * 3L + cls * L + i; fp64 or
+// rounded to fp32.
+__device__ inline void put_cs(double2* p, double2 v) { *p = v; }
+__device__ inline void put_cs(float2* p, double2 v) { *p = make_float2((float)v.x, (float)v.y); }
+
+template <typename T>
+__global__ void cf_query_table_kernel(T* __restrict__ tab, int L, int C, double inv_kappa,
                                       const double* __restrict__ theta) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x, cls = blockIdx.y, k = blockIdx.z;
   if (i < L)
-    tab[(int64_t)k * 3 * L + (int64_t)cls * L + i] = rope_cs(cf_query_pos(cls, i, C, inv_kappa), theta[k]);
+    put_cs(tab + (int64_t)k * 3 * L + (int64_t)cls * L + i, rope_cs(cf_query_pos(cls, i, C, inv_kappa), theta[k]));
+}
+
+template <typename T>
+static hipError_t cf_query_table(T* tab, int L, int D, int C, double inv_kappa, const double* theta,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(cf_query_table_kernel<T>, dim3((L + 255) / 256, 3, D / 2), dim3(256), 0, st, tab, L, C,
+                     inv_kappa, theta);
+  return hipGetLastError();
 }
 
 hipError_t launch_cf_query_table(double2* tab, int L, int D, int C, double inv_kappa, const double* theta,
                                  hipStream_t st) {
-  hipLaunchKernelGGL(cf_query_table_kernel, dim3((L + 255) / 256, 3, D / 2), dim3(256), 0, st, tab, L, C,
-                     inv_kappa, theta);
-  return hipGetLastError();
+  return cf_query_table(tab, L, D, C, inv_kappa, theta, st);
+}
+
+hipError_t launch_cf_query_table_f32(float2* tab, int L, int D, int C, double inv_kappa, const double* theta,
+                                     hipStream_t st) {
+  return cf_query_table(tab, L, D, C, inv_kappa, theta, st);
 }
 
 // ---- dca_rope_remap -----------------------------------------------------------------
