@@ -667,8 +667,9 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
     phase_barrier();
     phase_barrier();
   } else {
-    phase_barrier();
+    // the first query variant's loads overlap group 0's K(0) loads
     prep_q(vcur);
+    phase_barrier();
     do_qk(0);
     phase_barrier();
     VTile vprv = vcur;
