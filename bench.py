@@ -65,8 +65,9 @@ def source_hash(files):
 
 def measured_traffic(key):
     """HBM bytes per launch of kernel `key` ("prefill_attend", "prefill_prepare",
-    "decode_split" or "rope_remap") from the committed rocprofv3 counter runs,
-    or None when that kernel's source changed since they were taken."""
+    "decode_split", "rope_remap", "prefill_attend_16k" or "prefill_prepare_16k")
+    from the committed rocprofv3 counter runs, or None when that kernel's
+    source changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[key]
@@ -618,6 +619,8 @@ def main():
                                     "tflops": fl / ((prep + att) * 1e-3) / 1e12,
                                     "attend_tflops": fl / (att * 1e-3) / 1e12,
                                     "frac": fl / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "steps": n7,
+                                    "traffic": measured_traffic("prefill_attend_16k"),
+                                    "prepare_traffic": measured_traffic("prefill_prepare_16k"),
                                     "shape": {k_: P7[k_] for k_ in ("B", "L", "Hq", "Hkv", "D", "c", "w")}}
         if args.only == "prefill7b":
             result["value"], result["unit"] = result["prefill_16k_7b"]["tflops"], "TFLOP/s"
