@@ -18,7 +18,9 @@ Printed JSON (one line, stdout):
   rope_remap_100k  dca_rope_remap building the decode_100k key cache (GB/s)
   prefill_16k_7b   the DCA prefill of the Llama2-7B-shaped 16k workload (32/32 heads)
   prefill_128k the same prefill at 131072 tokens
-  cpu_baseline the fp64 oracle timed on a bounded sample of rows on the host
+  cpu_baseline the fp64 oracle timed on a bounded sample of rows on the host,
+               with whole oracle calls beside it (`full_oracle`: the tiny fp32
+               prefill, one decode_100k sequence)
 """
 from __future__ import annotations
 
@@ -185,6 +187,32 @@ def cpu_baseline(q, k, v, cfg, seconds):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
+def cpu_full_oracle(dec_one):
+    """Whole oracle calls, labelled: the tiny fp32 prefill (every row and
+    head) and, when `dec_one` holds it, one decode_100k sequence (q, raw K and
+    V of sequence 0)."""
+    import oracle
+    from long_context_attention_dca_amd import inputs
+    out = []
+    T = inputs.WORKLOADS["tiny_f32"]
+    q, k, v = inputs.prefill_inputs(T["B"], T["L"], T["Hq"], T["Hkv"], T["D"], "fp32", T["seed"])
+    t0 = time.perf_counter()
+    oracle.dca_prefill_ref(q, k, v, T["c"], T["w"], T["base"])
+    dt = time.perf_counter() - t0
+    out.append({"label": f"tiny_f32 whole prefill (B {T['B']}, L {T['L']}, Hq {T['Hq']}, D {T['D']}, every row)",
+                "seconds": dt, "value": prefill_flops(T["B"], T["L"], T["Hq"], T["D"]) / dt / 1e9, "unit": "GFLOP/s"})
+    if dec_one is not None:
+        DC = inputs.WORKLOADS["decode_100k"]
+        dq1, dk1, dv1 = dec_one
+        t0 = time.perf_counter()
+        oracle.dca_decode_ref(dq1, dk1, dv1, DC["c"], DC["w"], DC["base"])
+        dt = time.perf_counter() - t0
+        out.append({"label": f"decode_100k sequence 0 ({DC['kv_len']} cached keys, {DC['Hq']} query heads)",
+                    "seconds": dt, "value": decode_bytes(1, DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"]) / dt / 1e9,
+                    "unit": "GB/s"})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +292,7 @@ def main():
         log("generating decode_100k inputs")
         dq_h, dk_h, dv_h = inputs.decode_inputs(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"], "bf16",
                                                 DC["seed"])
+        dec_one = (dq_h[:1].clone(), dk_h[:1].clone(), dv_h[:1].clone())   # for the CPU baseline
         dq = dq_h.to(dev)
         kraw = dk_h.to(dev)
         if args.no_chunked:
@@ -701,6 +730,8 @@ def main():
     if run_prefill and not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(q_h, k_h, v_h, P, args.cpu_seconds)
+        log("cpu baseline: whole oracle calls (tiny fp32 prefill, one decode_100k sequence)")
+        result["cpu_baseline"]["full_oracle"] = cpu_full_oracle(dec_one if run_decode else None)
     print(json.dumps(result), flush=True)
 
 
