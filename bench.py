@@ -213,6 +213,68 @@ def cpu_full_oracle(dec_one):
     return out
 
 
+def first_calls(dev):
+    """Per-call times (HIP events) of the decode_100k call and the 32k
+    attention in the states where first calls were seen to run slow: a cache
+    or workspace just built, a new allocation filled by a copy, the same
+    buffers again, after an unrelated 3 GiB write, and after 2 s idle.  One
+    JSON line per series, with the shader clock read after each call."""
+    import torch
+    import long_context_attention_dca_amd as dca
+    from long_context_attention_dca_amd import inputs
+    clk = ClockSampler(dev)
+
+    def series(label, fn, n):
+        ms, mhz = [], []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(round(e0.elapsed_time(e1), 3))
+            mhz.append(clk._read() if clk.path else None)
+        print(json.dumps({"first_calls": label, "ms": ms, "mhz": mhz}), flush=True)
+
+    DC = inputs.WORKLOADS["decode_100k"]
+    dq, dk, dv = (x.to(dev) for x in inputs.decode_inputs(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"],
+                                                          "bf16", DC["seed"]))
+    kc = dca.rope_remap(dk, dca.DCA_MAP_KEY, DC["c"], DC["w"], DC["base"], 0)
+    del dk
+    ws = torch.empty(dca.decode_workspace_bytes(DC["B"], DC["kv_len"], DC["Hq"], DC["Hkv"], DC["D"], torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    dec = lambda kc_: dca.decode(dq, kc_, dv, DC["c"], DC["w"], DC["base"], workspace=ws)
+    torch.cuda.synchronize()
+    series("decode_100k, cache just built", lambda: dec(kc), 20)
+    kc2 = kc.clone()
+    torch.cuda.synchronize()
+    series("decode_100k, a new allocation filled by a copy", lambda: dec(kc2), 20)
+    series("decode_100k, the first cache again", lambda: dec(kc), 10)
+    junk = torch.empty(3 << 30, dtype=torch.uint8, device=dev)
+    junk.fill_(1)
+    torch.cuda.synchronize()
+    series("decode_100k, after an unrelated 3 GiB write", lambda: dec(kc), 10)
+    del junk
+    time.sleep(2.0)
+    series("decode_100k, after 2 s idle", lambda: dec(kc), 10)
+    del kc, kc2, dq, dv, ws
+    torch.cuda.empty_cache()
+    P = inputs.WORKLOADS["llama2_70b_32k"]
+    q, k, v = (x.to(dev) for x in inputs.prefill_inputs(P["B"], P["L"], P["Hq"], P["Hkv"], P["D"], "bf16", P["seed"]))
+    o = torch.empty_like(q)
+    nb = dca.prefill_workspace_bytes(P["B"], P["L"], P["Hkv"], P["D"], P["c"], torch.bfloat16)
+    w1, w2 = (torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(2))
+    att = lambda ws_: dca.prefill_attend(q, ws_, P["Hkv"], P["c"], P["w"], out=o)
+    dca.prefill_prepare(k, v, P["c"], P["w"], P["base"], workspace=w1)
+    torch.cuda.synchronize()
+    series("llama2_70b_32k attention, workspace just prepared", lambda: att(w1), 10)
+    dca.prefill_prepare(k, v, P["c"], P["w"], P["base"], workspace=w2)
+    torch.cuda.synchronize()
+    series("llama2_70b_32k attention, a second workspace just prepared", lambda: att(w2), 10)
+    time.sleep(2.0)
+    series("llama2_70b_32k attention, the first workspace after 2 s idle", lambda: att(w1), 8)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +296,9 @@ def main():
                     help="run one workload only (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--first-calls", action="store_true",
+                    help="only time decode_100k and 32k attention call by call on fresh allocations, "
+                         "after other traffic and after idle (where the slow first calls come from)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -258,6 +323,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}), flush=True)
+        return
+
+    if args.first_calls:
+        first_calls(dev)
         return
 
     P = inputs.WORKLOADS["llama2_70b_32k"]
