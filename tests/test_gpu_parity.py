@@ -53,10 +53,12 @@ def bf16_lse_bar(scale, qn, kmax):
     2^-8 per element), so a score q.k moves by at most
     ((1 + 2^-8)^2 - 1) * sum_d |q_d k_d| <= 2^-7 (1 + 2^-9) |q| |k| (rotations
     keep norms), times sm_scale; the LSE is 1-Lipschitz in the largest score
-    change.  The probabilities are rounded to bf16 before they are summed into
-    the normaliser, which moves ln l by at most -ln(1 - 2^-8) < 2^-8 (1 + 2^-8).
-    fp32 accumulation (dot products of 64-128 terms, a few thousand tile sums)
-    adds well under 1e-5 relative; 1e-4 absolute covers it."""
+    change.  The kernels sum the normaliser from the fp32 probabilities and
+    round them to bf16 only for the PV product; the 2^-8 term (what summing
+    the rounded ones would move ln l by, -ln(1 - 2^-8) < 2^-8 (1 + 2^-8)) is
+    kept as margin.  fp32 accumulation (dot products of 64-128 terms, a few
+    thousand tile sums) adds well under 1e-5 relative; 1e-4 absolute covers
+    it."""
     return 2.0 ** -7 * (1 + 2.0 ** -8) * scale * qn * kmax + 2.0 ** -8 * (1 + 2.0 ** -7) + 1e-4
 
 
