@@ -18,13 +18,13 @@ Sources (cited by page title and section):
       fixed-size chunks; the relation of a pair is decided by the chunk-index
       difference (0 = intra, 1 = successive, >= 2 = inter); intra pairs keep
       their true distance with no scaling; inter pairs keep the fine offset inside
-      the key's chunk and never exceed the pretrain window.
+      the key's chunk, and their distance stays below the pretrain length.
     - "Deep Dive", sub-section "1. Successive Chunk Smoothing": successive
       pairs see the plain local distance near the chunk edge and move
       continuously toward the inter-chunk value deeper into the chunk.
     - "End-to-End Implementation" script: causal pairs are those with i >= j
-      (the diagonal included), and the effective distance over the causal
-      half never exceeds the pretrain window.
+      (the diagonal included), and every causal pair's effective distance is
+      bounded by the pretrain length.
 * "LLM Maybe LongLM: Self-Extend LLM Context Window Without Tuning" code
   entry names ``rotate_half`` / ``apply_rotary_pos_emb`` / ``repeat_kv``:
   the rotate-half RoPE pairing and contiguous GQA head groups.
