@@ -119,9 +119,10 @@ int dca_rope_remap(const void* x, void* out, int64_t B, int64_t L, int64_t H, in
 
 /*
  * Scratch bytes dca_prefill needs for these sizes (0 on invalid sizes).
- * Holds the fp64 rope cos/sin table [c, D/2], the rotated keys (head-major,
- * padded to a multiple of 128 rows) and the values (bf16: tiled transpose;
- * fp32: a copy).
+ * Holds the query cos/sin table of positions [0, c) (16 bytes reserved per
+ * position and frequency: bf16 stores fp32 pairs frequency-major, fp32 fp64
+ * pairs), the rotated keys (head-major, padded to a multiple of 128 rows)
+ * and the values (bf16: tiled transpose; fp32: a copy).
  */
 size_t dca_prefill_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D, int c,
                                    int dtype);
@@ -147,8 +148,9 @@ size_t dca_prefill_workspace_bytes(int64_t B, int64_t L, int64_t Hkv, int64_t D,
  *   sm_scale  : softmax scale; <= 0 selects 1/sqrt(D).
  *   ws        : scratch of at least dca_prefill_workspace_bytes(...) bytes.
  * bf16 runs QK^T and PV on bf16 MFMA with fp32 accumulation (rotated q/k and
- * the probabilities are rounded to bf16 before each product); fp32 runs in
- * fp32 throughout.
+ * the probabilities are rounded to bf16 before each product; keys are
+ * rotated in fp64, queries in fp32 from fp32 angles; the softmax normaliser
+ * sums the fp32 probabilities); fp32 runs in fp32 throughout.
  */
 int dca_prefill(const void* q, const void* k, const void* v, void* o, float* lse, void* k_rot_out,
                 int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int c, int w,
@@ -159,7 +161,7 @@ int dca_prefill(const void* q, const void* k, const void* v, void* o, float* lse
  * The two phases dca_prefill runs, exposed so a caller can prepare K/V once
  * and time or repeat the attention phase on its own.
  *
- * dca_prefill_prepare: builds, inside ws, the fp64 cos/sin table for positions
+ * dca_prefill_prepare: builds, inside ws, the query cos/sin table for positions
  * [0, c), the keys rotated at j mod s (head-major, rows padded to a multiple
  * of 128) and the value layout the attention kernel reads (bf16: a tiled
  * transpose; fp32: a copy).  k_rot_out as in dca_prefill (may be NULL).
@@ -194,11 +196,13 @@ int dca_prefill_attend(const void* q, void* o, float* lse, int64_t B, int64_t L,
  * query position minus a key position:
  *   keys at j (same or adjacent chunk) or at c_j C / kappa + o_j (older);
  *   queries at i, i - o_i (1 - 1/kappa) or c_i C / kappa + o_i.
- * These positions and their cos / sin are evaluated in fp64.
+ * These positions and their cos / sin are evaluated in fp64 (for bf16 the
+ * query angles are then rounded to fp32).
  *
- * dca_coarse_fine_workspace_bytes: scratch for the fp64 theta table, the fp64
+ * dca_coarse_fine_workspace_bytes: scratch for the fp64 theta table, the
  * (cos, sin) of the three query positions of every row (3 * L * D/2 * 16
- * bytes), the two key rotations and the V layout (0 on invalid sizes).
+ * bytes reserved: fp64 pairs, or fp32 pairs for bf16), the two key rotations
+ * and the V layout (0 on invalid sizes).
  * dca_coarse_fine_prefill: q [B, L, Hq, D], k / v [B, L, Hkv, D] raw; o, lse,
  *   sm_scale, GQA, dtypes as in dca_prefill.  chunk >= 1, train_len >= 1,
  *   target_len >= 1.  bf16 needs chunk to be a multiple of 64, so that every
@@ -265,7 +269,8 @@ int dca_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, v
  * Softmax, scale, LSE, GQA, layouts and dtypes as in dca_prefill.
  *
  * dca_selfextend_workspace_bytes: scratch bytes for these sizes (0 on invalid
- * sizes): the fp64 cos/sin table for every position used, the keys rotated at
+ * sizes): the cos/sin table for every position used (fp64; bf16 keeps fp32
+ * query pairs there and makes the keys' angles in the kernel), the keys rotated at
  * j and at floor(j/G) (head-major, rows padded to a multiple of 128) and the
  * value layout (bf16: tiled transpose; fp32: a copy).
  *
