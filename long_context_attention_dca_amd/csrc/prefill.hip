@@ -561,17 +561,24 @@ prefill_bf16_pp_kernel(PrefillArgs a, int nqt, int xcd_map, float scale_log2) {
   // The query variant of virtual tile v, re-made when it changes.  Split map:
   // each lane's own class (rows of one wave can span a chunk boundary); the
   // wave re-makes its variants when any lane's class changes.
+  // DCA: a row whose successive position min(s + r, c - 1) is already c - 1
+  // (r >= w - 1) has the same successive and inter variant, so a wave whose
+  // rows all have that property keeps its registers when the relation moves
+  // from inter to successive.
+  auto same_pos = [&](int c1, int c2) __attribute__((always_inline)) {
+    return c2 >= 0 && query_pos(c1, rq_l, s, c) == query_pos(c2, rq_l, s, c);
+  };
   auto prep_q = [&](const VTile& v) __attribute__((always_inline)) {
     if constexpr (MAP == kMapDCASplit) {
       const int cls = min(max(nq_l - v.nk, 0), 2);
       if (__any(cls != cur_cls)) {
-        load_q(cls);
+        if (!__all(same_pos(cls, cur_cls))) load_q(cls);
         cur_cls = cls;
       }
     } else {
       const int cls = class_of(v.t);
       if (cls != cur_cls) {
-        load_q(cls);
+        if (MAP != kMapDCA || !__all(same_pos(cls, cur_cls))) load_q(cls);
         cur_cls = cls;
       }
     }
