@@ -13,7 +13,7 @@
 //
 // One bf16 kernel, the two-group "ping-pong" kernel below, serves every map
 // (DCA with any chunk size and query offset, SelfExtend, the guide's coarse /
-// fine map); fp32 inputs take a plain VALU kernel.  Common to both bf16 paths:
+// fine map); fp32 inputs take a plain VALU kernel.  The bf16 kernel:
 //   * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
 //     wave's 32 rotated queries held in registers.  In the 32x32 output layout
 //     each lane owns one query column, so the row max / sum need a single
@@ -25,8 +25,9 @@
 //     global->LDS buffer loads (no staging registers); rows padded by 16 bytes
 //     make the MFMA fragment reads bank-conflict free with immediate offsets.
 //   * The query variant lives in registers and is re-made (rotate raw Q with the
-//     cos/sin table) only when the tile relation changes: inter -> successive
-//     -> intra, at most three times per row.
+//     fp32 cos/sin table) only when the tile relation changes: inter ->
+//     successive -> intra, at most three times per row, and not at all for
+//     inter -> successive where both positions are c - 1.
 //   * Online softmax in the log2 domain with a lazy rescale.
 //   * Workgroups are ordered longest causal row first, and, when B*Hkv is a
 //     multiple of 8, mapped so that each XCD (workgroup id mod 8) serves whole
