@@ -73,3 +73,18 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in r.stderr or "1 GPU" in r.stderr or "single" in r.stderr, r.stderr
+
+
+def test_cpu_full_oracle_labels_whole_calls(bench):
+    # the tiny fp32 prefill is timed whole and labelled; the decode sequence
+    # only when one is handed over (here a small stand-in of the same form)
+    out = bench.cpu_full_oracle(None)
+    assert len(out) == 1 and out[0]["label"].startswith("tiny_f32 whole prefill")
+    assert out[0]["seconds"] > 0 and out[0]["value"] > 0 and out[0]["unit"] == "GFLOP/s"
+    import torch
+    g = torch.Generator().manual_seed(0)
+    dq = torch.randn(1, 64, 128, generator=g).to(torch.bfloat16)
+    dk = torch.randn(1, 300, 8, 128, generator=g).to(torch.bfloat16)
+    dv = torch.randn(1, 300, 8, 128, generator=g).to(torch.bfloat16)
+    out = bench.cpu_full_oracle((dq, dk, dv))
+    assert len(out) == 2 and out[1]["label"].startswith("decode_100k sequence 0") and out[1]["unit"] == "GB/s"
