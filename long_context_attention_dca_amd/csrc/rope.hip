@@ -10,6 +10,8 @@
 #include "dca_common.hpp"
 #include "dca_launch.hpp"
 
+#include <mutex>
+
 namespace dca {
 
 // ---- cos/sin table (fp64), [npos][D/2] or frequency-major [D/2][npos] -------------------
@@ -180,6 +182,45 @@ __device__ inline void rotate_pairs(float* x1, float* x2, const double2* cs) {
   }
 }
 
+// The bf16 form of rotate_pairs on packed bf16 words (2 values each), with
+// the same results and fewer operations.  The fp64 value y goes to fp32
+// (round to nearest even) and then to bf16.  The two roundings equal the
+// single one except when the fp32 value is itself a midpoint between two bf16
+// numbers (low 16 bits 0x8000) without being y: a value on either side of a
+// bf16 midpoint cannot cross it when rounded to fp32, since the midpoint is an
+// fp32 number.  Where any active lane of the wave meets that case (about one
+// value in 65536), the whole wave redoes its pairs through rotate_pairs'
+// round-to-odd step instead.
+template <int W>
+__device__ inline void rotate_bf16_words(const uint32_t* w1, const uint32_t* w2, const double2* cs, uint32_t* o1,
+                                         uint32_t* o2) {
+  constexpr int N = 2 * W;
+  float f1[N], f2[N];
+  uint64_t midpoint = 0;   // lanes with an fp32 value on a bf16 midpoint (one compare per value)
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const double a = __uint_as_float(e & 1 ? w1[e / 2] & 0xffff0000u : w1[e / 2] << 16);
+    const double b = __uint_as_float(e & 1 ? w2[e / 2] & 0xffff0000u : w2[e / 2] << 16);
+    f1[e] = (float)fma(a, cs[e].x, -(b * cs[e].y));
+    f2[e] = (float)fma(b, cs[e].x, a * cs[e].y);
+    midpoint |= __builtin_amdgcn_ballot_w64((__float_as_uint(f1[e]) & 0xffffu) == 0x8000u);
+    midpoint |= __builtin_amdgcn_ballot_w64((__float_as_uint(f2[e]) & 0xffffu) == 0x8000u);
+  }
+  if (midpoint != 0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      f1[e] = __uint_as_float(e & 1 ? w1[e / 2] & 0xffff0000u : w1[e / 2] << 16);
+      f2[e] = __uint_as_float(e & 1 ? w2[e / 2] & 0xffff0000u : w2[e / 2] << 16);
+    }
+    rotate_pairs<uint16_t, N>(f1, f2, cs);
+  }
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    o1[q] = pack_bf16x2(f1[2 * q], f1[2 * q + 1]);
+    o2[q] = pack_bf16x2(f2[2 * q], f2[2 * q + 1]);
+  }
+}
+
 constexpr int kRemapTokens = 4;
 
 template <typename T, int D>
@@ -211,12 +252,21 @@ __global__ void __launch_bounds__(256) rope_remap_kernel(const T* __restrict__ x
   for (; b < B;) {
     const int g = r % NG, th = r / NG, h = th % H, tk = th / H;
     const int64_t off = ((b * L + t0 + tk) * H + h) * D + g * N;
-    float x1[N], x2[N];
-    Vec16<T>::unpack(load_stream((const uint4*)(x + off)), x1);
-    Vec16<T>::unpack(load_stream((const uint4*)(x + off + half)), x2);
-    rotate_pairs<T, N>(x1, x2, &cs[tk][g * N]);
-    store_stream((uint4*)(out + off), Vec16<T>::pack(x1));
-    store_stream((uint4*)(out + off + half), Vec16<T>::pack(x2));
+    const uint4 u1 = load_stream((const uint4*)(x + off)), u2 = load_stream((const uint4*)(x + off + half));
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w}, w2[4] = {u2.x, u2.y, u2.z, u2.w};
+      uint32_t o1[4], o2[4];
+      rotate_bf16_words<4>(w1, w2, &cs[tk][g * N], o1, o2);
+      store_stream((uint4*)(out + off), make_uint4(o1[0], o1[1], o1[2], o1[3]));
+      store_stream((uint4*)(out + off + half), make_uint4(o2[0], o2[1], o2[2], o2[3]));
+    } else {
+      float x1[N], x2[N];
+      Vec16<T>::unpack(u1, x1);
+      Vec16<T>::unpack(u2, x2);
+      rotate_pairs<T, N>(x1, x2, &cs[tk][g * N]);
+      store_stream((uint4*)(out + off), Vec16<T>::pack(x1));
+      store_stream((uint4*)(out + off + half), Vec16<T>::pack(x2));
+    }
     b += step_b;
     r += step_r;
     if (r >= inner) {
@@ -301,168 +351,264 @@ __global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
   }
 }
 
-// bf16 prepare pass with 16-byte accesses throughout.  One workgroup per
-// (64-key tile, group of up to kPrepHeads KV heads, sequence).  A thread owns
-// (key row, 8-dim group) items: it gets the item's cos/sin once and applies
-// them to every head of the group.  The V rows of all the group's heads are
-// loaded before the key work, so their loads are in flight meanwhile, then
-// each head's tile is transposed through LDS and written as whole 16-byte
-// runs of 8 keys (in the key order of vt_perm).
-constexpr int kPrepHeads = 2;
+// bf16 prepare pass.  Every wave works through its own share of a flat list of
+// units in which K and V units are interleaved in proportion, so that the
+// reads, the writes and the K rotation's fp64 arithmetic of different waves
+// overlap; no wave waits for another.
+//  * K unit: RK consecutive key rows (RK = 256 / D: 2 for D 128, 4 for
+//    D 64) of one sequence and up to kPrepKeyHeads KV heads.  A lane owns one
+//    row and 2 frequencies: it makes their cos/sin pairs once and turns those
+//    pairs in every head of the unit (4-byte loads and stores; 32 lanes cover
+//    a half row, one 128-byte run).
+//  * V unit: 64 keys x 64 dims of one head.  The wave writes the rows into
+//    its own LDS rows transposed (one LDS row per dim, keys in the order of
+//    vt_perm), then stores each dim's 64 keys as 16-byte runs of 8: whole
+//    128-byte lines of the V^T tile.
+// The grid is twice the workgroups that fit on the chip at once; wave w takes
+// units w, w + W, w + 2W, ... (W waves in all).
+constexpr int kPrepKeyHeads = 8;
+constexpr int kPrepKeyWords = 1;   // 32-bit words (2 frequencies each) per lane and half row
+constexpr int kPrepVKeys = 64;     // keys per V unit
+constexpr int kPrepVRow = kPrepVKeys + 8;   // LDS row of a V unit (one dim), bf16
 
-template <int D>
-__global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a) {
-  constexpr int half = D / 2, NG = half / 8;             // 8-dim groups per half row
-  constexpr int TK = kPrefillTileKeys;
-  constexpr int KITEMS = TK * NG / 256;                  // key items per thread
-  constexpr int VG = D / 8;                              // 8-dim groups per V row
-  constexpr int VITEMS = TK * VG / 256;                  // V loads per thread and head
-  constexpr int OITEMS = D * (TK / 8) / 256;             // V^T stores per thread and head
-  static_assert(KITEMS >= 1 && VITEMS >= 1 && OITEMS >= 1, "tile too small for the workgroup");
-  const int tile = blockIdx.x, b = blockIdx.z, h0 = blockIdx.y * kPrepHeads;
-  const int nh = a.Hkv - h0 < kPrepHeads ? a.Hkv - h0 : kPrepHeads;
-  const int j0 = tile * TK;
-  const int Lb = a.per_seq ? a.seq_len[b] : a.L;   // valid rows of this sequence
-  const uint16_t* k = (const uint16_t*)a.k;
-  const uint16_t* vv = (const uint16_t*)a.v;
-  const bool with_v = a.vt != nullptr;
-  const bool rotate = a.table != nullptr || a.pos_mode != 0;
-  // pos_mode 2: theta_k once per workgroup, as the table kernel makes it
+// NW consecutive 32-bit words with the non-temporal hint / a plain store.
+template <int NW>
+__device__ inline void load_words(const uint16_t* p, uint32_t* w) {
+  if constexpr (NW == 1) {
+    w[0] = __builtin_nontemporal_load((const uint32_t*)p);
+  } else {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = __builtin_nontemporal_load((const u32x2*)p);
+    w[0] = t[0];
+    w[1] = t[1];
+  }
+}
+template <int NW>
+__device__ inline void store_words(uint16_t* p, const uint32_t* w) {
+  if constexpr (NW == 1)
+    *(uint32_t*)p = w[0];
+  else
+    *(uint2*)p = make_uint2(w[0], w[1]);
+}
+// LDS written by some lanes of this wave, then read by others.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// PM: 0 = copy (keys already rotated), 1 = real positions from a.theta
+// (pos_mode 1), 2 = cos/sin made here from a.base (pos_mode 2).
+template <int D, int PM, bool PAGED>
+__global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a, int64_t nK, int64_t nV) {
+  constexpr int half = D / 2, NW = kPrepKeyWords, NF = 2 * NW, NKG = half / NF, RK = 64 / NKG, ND = D / 64;
+  constexpr int KH = kPrepKeyHeads;
+  constexpr bool rotate = PM != 0;
   __shared__ double theta_s[half];
-  if (a.pos_mode == 2) {
+  __shared__ __attribute__((aligned(16))) uint16_t vsh[4][64][kPrepVRow];
+  if (PM == 2) {
     if (threadIdx.x < half) theta_s[threadIdx.x] = pow(a.base, -2.0 * (double)threadIdx.x / (double)D);
     __syncthreads();
   }
-
-  // V rows of every head of the group (zero past the valid rows and for
-  // unreadable pages).
-  uint4 vr[kPrepHeads][VITEMS];
-  if (with_v) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * 4, N = nK + nV;
+  const uint16_t* kin = (const uint16_t*)a.k;
+  const uint16_t* vin = (const uint16_t*)a.v;
+  const int nRG = a.Lp / RK, nHG = (a.Hkv + KH - 1) / KH, nT = a.Lp / kPrefillTileKeys;
+  const int64_t rowstride = (int64_t)a.Hkv * D;   // elements per input row
+  for (int64_t u = (int64_t)blockIdx.x * 4 + wave; u < N; u += W) {
+    // the lane index is re-read per unit so that the compiler does not keep
+    // both unit kinds' lane offsets in registers across the loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int64_t kc = u * nK / N;   // K units before unit u
+    if ((u + 1) * nK / N > kc) {
+      // ---- K unit kc: (sequence b, row group g, head group hg)
+      const int hg = (int)(kc % nHG);
+      const int64_t bg = kc / nHG;
+      const int g = (int)(bg % nRG), b = (int)(bg / nRG);
+      const int r = lane / NKG, k0 = (lane % NKG) * NF;
+      const int j = g * RK + r;
+      const int Lb = a.per_seq ? a.seq_len[b] : a.L;   // valid rows of this sequence
+      const int h0 = hg * KH, nh = a.Hkv - h0 < KH ? a.Hkv - h0 : KH;
+      const int64_t crow = PAGED ? (j < Lb ? cache_row(a.pg, a.in_rows, b, j) : 0) : (int64_t)b * a.in_rows + j;
+      const bool valid = j < Lb && crow >= 0;
+      double2 cs[NF];
+      if (rotate && valid) {
+        if (PM == 1) {
+          const double pos = (double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk);
 #pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int item = threadIdx.x + it * 256;
-      const int row = item / VG, dg = item - row * VG;
-      const int j = j0 + row;
-      const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : -1;
+          for (int e = 0; e < NF; ++e) cs[e] = rope_cs(pos, a.theta[k0 + e]);
+        } else {
+          const double pos = (double)((j / a.kdiv) % a.kmod);
 #pragma unroll
-      for (int hh = 0; hh < kPrepHeads; ++hh)
-        vr[hh][it] = (hh < nh && crow >= 0) ? load_stream((const uint4*)(vv + (crow * a.Hkv + h0 + hh) * D + dg * 8))
-                                            : make_uint4(0, 0, 0, 0);
+          for (int e = 0; e < NF; ++e) {
+            double sn, cn;
+            sincos(pos * theta_s[k0 + e], &sn, &cn);
+            cs[e] = make_double2(cn, sn);
+          }
+        }
+      }
+      // the angles first, then the loads: their registers are not live together
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* src;
+      if (PAGED) {
+        src = kin + (crow * a.Hkv + h0) * D + k0;
+      } else {   // wave-uniform base + 32-bit lane offset
+        const uint16_t* base = kin + ((int64_t)b * a.in_rows + (int64_t)g * RK) * rowstride + h0 * D;
+        src = base + (uint32_t)(r * rowstride + k0);
+      }
+      uint32_t x1[KH][NW], x2[KH][NW];
+#pragma unroll
+      for (int hh = 0; hh < KH; ++hh)
+        if (hh < nh && valid) {
+          load_words<NW>(src + hh * D, x1[hh]);
+          load_words<NW>(src + hh * D + half, x2[hh]);
+        }
+      uint16_t* dst = (uint16_t*)a.krot + (((int64_t)b * a.Hkv + h0) * a.Lp + (int64_t)g * RK) * D + r * D + k0;
+      const uint32_t nan2 = 0x7fc07fc0u;   // two bf16 quiet NaNs
+#pragma unroll
+      for (int hh = 0; hh < KH; ++hh) {
+        if (hh >= nh) continue;
+        uint32_t y1[NW], y2[NW];
+        if (j >= Lb) {
+#pragma unroll
+          for (int q = 0; q < NW; ++q) y1[q] = y2[q] = 0;
+        } else if (!valid) {   // unreadable page: poison the key so the rows using it give NaN
+#pragma unroll
+          for (int q = 0; q < NW; ++q) y1[q] = y2[q] = nan2;
+        } else if (rotate) {
+          rotate_bf16_words<NW>(x1[hh], x2[hh], cs, y1, y2);
+          if (a.k_rot_out) {
+            uint16_t* ko = (uint16_t*)a.k_rot_out + (crow * a.Hkv + h0 + hh) * D + k0;
+            store_words<NW>(ko, y1);
+            store_words<NW>(ko + half, y2);
+          }
+        } else {   // already rotated: exact copy
+#pragma unroll
+          for (int q = 0; q < NW; ++q) {
+            y1[q] = x1[hh][q];
+            y2[q] = x2[hh][q];
+          }
+        }
+        uint16_t* d = dst + (int64_t)hh * a.Lp * D;
+        store_words<NW>(d, y1);
+        store_words<NW>(d + half, y2);
+      }
+    } else {
+      // ---- V unit u - kc: (sequence b, 64-key tile t, head h, dims dh * 64.., keys kh * 32..)
+      constexpr int NKH = kPrefillTileKeys / kPrepVKeys, VL = kPrepVKeys / 8;
+      int64_t vv = u - kc;
+      const int kh = (int)(vv % NKH);
+      vv /= NKH;
+      const int dh = (int)(vv % ND);
+      vv /= ND;
+      const int h = (int)(vv % a.Hkv);
+      vv /= a.Hkv;
+      const int t = (int)(vv % nT), b = (int)(vv / nT);
+      const int Lb = a.per_seq ? a.seq_len[b] : a.L;
+      const int jb = t * kPrefillTileKeys + kh * kPrepVKeys;
+      // zero past the valid rows and for unreadable pages
+      uint4 x[VL];
+#pragma unroll
+      for (int it = 0; it < VL; ++it) {
+        const int i = lane + it * 64, row = i >> 3, dg = i & 7;
+        const int j = jb + row;
+        if (PAGED) {
+          const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : -1;
+          x[it] = crow >= 0 ? load_stream((const uint4*)(vin + (crow * a.Hkv + h) * D + dh * 64 + dg * 8))
+                            : make_uint4(0, 0, 0, 0);
+        } else {
+          const uint16_t* base = vin + ((int64_t)b * a.in_rows + jb) * rowstride + h * D + dh * 64;
+          x[it] = j < Lb ? load_stream((const uint4*)(base + (uint32_t)(row * rowstride + dg * 8)))
+                         : make_uint4(0, 0, 0, 0);
+        }
+      }
+      uint16_t(*vs)[kPrepVRow] = vsh[wave];
+#pragma unroll
+      for (int it = 0; it < VL; ++it) {
+        const int i = lane + it * 64, row = i >> 3, dg = i & 7;
+        const int slot = vt_perm(row);
+        const uint32_t w4[4] = {x[it].x, x[it].y, x[it].z, x[it].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vs[dg * 8 + 2 * q][slot] = (uint16_t)(w4[q] & 0xffffu);
+          vs[dg * 8 + 2 * q + 1][slot] = (uint16_t)(w4[q] >> 16);
+        }
+      }
+      wave_lds_sync();
+      uint16_t* dst = (uint16_t*)a.vt + ((((int64_t)b * a.Hkv + h) * nT + t) * D + dh * 64) * kPrefillTileKeys +
+                      kh * kPrepVKeys;
+#pragma unroll
+      for (int it = 0; it < VL; ++it) {
+        const int i = lane + it * 64, dl = i / VL, kg = i % VL;
+        *(uint4*)(dst + dl * kPrefillTileKeys + kg * 8) = *(const uint4*)&vs[dl][kg * 8];
+      }
+      wave_lds_sync();   // this unit's LDS reads come before the next unit's writes
     }
   }
 
-  // Keys.
-#pragma unroll
-  for (int it = 0; it < KITEMS; ++it) {
-    const int item = threadIdx.x + it * 256;
-    const int row = item / NG, kg = item - row * NG;
-    const int j = j0 + row, k0 = kg * 8;
-    const int64_t crow = j < Lb ? cache_row(a.pg, a.in_rows, b, j) : 0;
-    const bool valid = j < Lb && crow >= 0;
-    uint4 x1[kPrepHeads], x2[kPrepHeads];
-#pragma unroll
-    for (int hh = 0; hh < kPrepHeads; ++hh)
-      if (hh < nh && valid) {
-        const uint16_t* src = k + (crow * a.Hkv + h0 + hh) * D + k0;
-        x1[hh] = load_stream((const uint4*)src);
-        x2[hh] = load_stream((const uint4*)(src + half));
-      }
-    double2 cs[8];
-    if (valid && rotate) {
-      if (a.pos_mode == 1) {
-        const double pos = (double)(j / a.cf_chunk) * a.cf_step + (double)(j % a.cf_chunk);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = rope_cs(pos, a.theta[k0 + e]);
-      } else if (a.pos_mode == 2) {
-        const double pos = (double)((j / a.kdiv) % a.kmod);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          double sn, cn;
-          sincos(pos * theta_s[k0 + e], &sn, &cn);
-          cs[e] = make_double2(cn, sn);
-        }
-      } else {
-        const double2* t = a.table + (int64_t)((j / a.kdiv) % a.kmod) * half + k0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = t[e];
-      }
-    }
-    const uint32_t nan2 = 0x7fc07fc0u;   // two bf16 quiet NaNs
-#pragma unroll
-    for (int hh = 0; hh < kPrepHeads; ++hh) {
-      if (hh >= nh) continue;
-      uint16_t* dst = (uint16_t*)a.krot + (((int64_t)b * a.Hkv + h0 + hh) * a.Lp + j) * D + k0;
-      uint4 y1, y2;
-      if (j >= Lb) {
-        y1 = y2 = make_uint4(0, 0, 0, 0);
-      } else if (crow < 0) {   // unreadable page: poison the key so the rows using it give NaN
-        y1 = y2 = make_uint4(nan2, nan2, nan2, nan2);
-      } else if (rotate) {
-        float f1[8], f2[8];
-        unpack_bf16x8(x1[hh], f1);
-        unpack_bf16x8(x2[hh], f2);
-        rotate_pairs<uint16_t, 8>(f1, f2, cs);
-        y1 = pack_bf16x8(f1);
-        y2 = pack_bf16x8(f2);
-        if (a.k_rot_out) {
-          uint16_t* ko = (uint16_t*)a.k_rot_out + (crow * a.Hkv + h0 + hh) * D + k0;
-          *(uint4*)ko = y1;
-          *(uint4*)(ko + half) = y2;
-        }
-      } else {   // already rotated: exact copy
-        y1 = x1[hh];
-        y2 = x2[hh];
-      }
-      *(uint4*)dst = y1;
-      *(uint4*)(dst + half) = y2;
-    }
-  }
-
-  // pos_mode 2: this launch also writes the cos / sin table of positions
+  // PM 2: this launch also writes the cos / sin table of positions
   // 0 .. table_rows - 1 in fp32, frequency-major ([D/2][table_rows]), a slice
-  // per workgroup.
-  if (a.pos_mode == 2 && a.table_out) {
-    const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-    const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-    const int64_t n = (int64_t)a.table_rows * half;
-    for (int64_t idx = wg * 256 + threadIdx.x; idx < n; idx += nwg * 256) {
+  // per wave.
+  if (PM == 2 && a.table_out) {
+    const int n = a.table_rows * half;
+    for (int64_t idx = ((int64_t)blockIdx.x * 4 + wave) * 64 + (threadIdx.x & 63); idx < n; idx += W * 64) {
       const int kk = (int)(idx / a.table_rows), p = (int)(idx - (int64_t)kk * a.table_rows);
       double sn, cn;
       sincos((double)p * theta_s[kk], &sn, &cn);
       a.table_out[idx] = make_float2((float)cn, (float)sn);
     }
   }
+}
 
-  // V^T tiles, one head at a time through LDS.
-  if (!with_v) return;
-  __shared__ __attribute__((aligned(16))) uint16_t vs[TK][D + 8];
-  const int ntiles = a.Lp / TK;
-  for (int hh = 0; hh < nh; ++hh) {
-    if (hh > 0) __syncthreads();   // the previous head's reads are done
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int item = threadIdx.x + it * 256;
-      const int row = item / VG, dg = item - row * VG;
-      uint4 u = vr[0][it];
-#pragma unroll
-      for (int x = 1; x < kPrepHeads; ++x)
-        if (x == hh) u = vr[x][it];
-      *(uint4*)&vs[row][dg * 8] = u;
-    }
-    __syncthreads();
-    uint16_t* dst = (uint16_t*)a.vt + ((((int64_t)b * a.Hkv + h0 + hh) * ntiles + tile) * D) * TK;
-#pragma unroll
-    for (int it = 0; it < OITEMS; ++it) {
-      const int item = threadIdx.x + it * 256;
-      const int d = item / (TK / 8), kg = item - d * (TK / 8);
-      uint16_t e[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) e[x] = vs[vt_perm(kg * 8 + x)][d];
-      *(uint4*)(dst + d * TK + kg * 8) =
-          make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
-                     e[6] | ((uint32_t)e[7] << 16));
-    }
+// Workgroups of a kernel that fit on the current device at once (cached per
+// device and kernel).
+constexpr int kMaxPrepDevices = 64;
+std::mutex g_prep_grid_mutex;
+
+template <typename K>
+static hipError_t resident_workgroups(K kernel, int* out) {
+  static int cache[kMaxPrepDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxPrepDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_prep_grid_mutex);
+  if (cache[dev] == 0) {
+    int per_cu = 0, ncu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[dev] = per_cu * ncu > 0 ? per_cu * ncu : 1;
   }
+  *out = cache[dev];
+  return hipSuccess;
+}
+
+template <int D, int PM, bool PAGED>
+static hipError_t launch_prep_bf16(const KvPrepArgs& a, hipStream_t st) {
+  constexpr int half = D / 2, RK = 64 / (half / (2 * kPrepKeyWords)), ND = D / 64;
+  const int64_t nK = (int64_t)a.B * (a.Lp / RK) * ((a.Hkv + kPrepKeyHeads - 1) / kPrepKeyHeads);
+  const int64_t nV = a.vt ? (int64_t)a.B * (a.Lp / kPrefillTileKeys) * a.Hkv * ND * (kPrefillTileKeys / kPrepVKeys) : 0;
+  int resident = 0;
+  const hipError_t e = resident_workgroups(kv_prep_bf16_kernel<D, PM, PAGED>, &resident);
+  if (e != hipSuccess) return e;
+  const int64_t need = (nK + nV + 3) / 4;
+  int64_t grid = 2 * (int64_t)resident;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((kv_prep_bf16_kernel<D, PM, PAGED>), dim3((unsigned)grid), dim3(256), 0, st, a, nK, nV);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prep_bf16_d(const KvPrepArgs& a, hipStream_t st) {
+  const bool paged = a.pg.bt != nullptr;
+  if (a.pos_mode == 1) return paged ? launch_prep_bf16<D, 1, true>(a, st) : launch_prep_bf16<D, 1, false>(a, st);
+  if (a.pos_mode == 2) return paged ? launch_prep_bf16<D, 2, true>(a, st) : launch_prep_bf16<D, 2, false>(a, st);
+  return paged ? launch_prep_bf16<D, 0, true>(a, st) : launch_prep_bf16<D, 0, false>(a, st);
 }
 
 hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st) {
@@ -472,15 +618,11 @@ hipError_t launch_kv_prep(const KvPrepArgs& a, int dtype, hipStream_t st) {
       hipLaunchKernelGGL((kv_prep_f32_kernel<64>), grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((kv_prep_f32_kernel<128>), grid, dim3(256), 0, st, a);
-  } else {
-    const dim3 grid((unsigned)(a.Lp / kPrefillTileKeys), (unsigned)((a.Hkv + kPrepHeads - 1) / kPrepHeads),
-                    (unsigned)a.B);
-    if (a.D == 64)
-      hipLaunchKernelGGL((kv_prep_bf16_kernel<64>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((kv_prep_bf16_kernel<128>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  // the bf16 pass takes its angles from a.base or a.theta, never a table
+  if (a.table != nullptr) return hipErrorInvalidValue;
+  return a.D == 64 ? launch_prep_bf16_d<64>(a, st) : launch_prep_bf16_d<128>(a, st);
 }
 
 }  // namespace dca
