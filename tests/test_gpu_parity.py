@@ -112,6 +112,27 @@ def test_rope_remap_all_maps(dtype, D, pos0):
     assert torch.equal(y, dca.rope_remap(xg, dca.DCA_MAP_KEY, c, w, 1e4, pos0))
 
 
+def test_rope_remap_rounds_once():
+    # The bf16 remap (and the prepare pass, bit-identical to it) returns the
+    # fp64 rotation rounded once to bf16, so it lies within half a bf16 ulp of
+    # the oracle's rotation, up to the fp64 differences between the two angle
+    # evaluations (1e-11 of the pair's magnitude covers them).  Rounding
+    # through fp32 without the midpoint repair would exceed half an ulp on
+    # the values whose fp32 rounding lands on a bf16 midpoint; the input is
+    # large enough to hold many of those.
+    c, w = 4096, 1024
+    x = inputs.prefill_inputs(4, 2048, 8, 8, 128, torch.bfloat16, seed=21, qk_scale=1.0)[0]
+    got = to_np(dca.rope_remap(x.to(dev()), dca.DCA_MAP_KEY, c, w, 1e4))
+    want = oracle.rope_remap_ref(x, 0, oracle.MAP_KEY, c, w, 1e4)
+    xf = to_np(x)
+    m = np.abs(xf[..., :64]) + np.abs(xf[..., 64:])
+    tol = 0.5 * bf16_ulp(want) + 1e-11 * np.concatenate([m, m], axis=-1)
+    err = np.abs(got - want)
+    assert np.all(err <= tol), (err - tol).max()
+    mid = (want.astype(np.float32).view(np.uint32) & 0xFFFF) == 0x8000
+    assert np.count_nonzero(mid) >= 20, np.count_nonzero(mid)
+
+
 @pytest.mark.parametrize("B,L,H", [(17, 5, 64), (1, 1, 1), (3, 9, 2), (2, 130, 40)])
 def test_rope_remap_shapes(B, L, H):
     # token counts that are not multiples of the 4 tokens a workgroup takes,
@@ -150,10 +171,13 @@ SMALL = [
     ("bf16_s64_L1", 1, 1, 2, 1, 128, 64, 0, torch.bfloat16, 2.0),
     ("bf16_s64_L300", 1, 300, 2, 2, 128, 100, 36, torch.bfloat16, 2.0),
     ("bf16_s256_L257", 3, 257, 2, 1, 64, 320, 64, torch.bfloat16, 2.0),
-    # KV head counts that leave the prepare pass's last 4-head group partly empty
+    # KV head counts that leave the prepare pass's last 8-head group partly
+    # empty: one group (6, 5, 3 heads) and a full group plus a partial one (12)
     ("bf16_hkv6_gqa2", 1, 400, 12, 6, 128, 192, 64, torch.bfloat16, 2.0),
     ("bf16_hkv5_mha_d64", 2, 250, 5, 5, 64, 128, 0, torch.bfloat16, 2.0),
     ("bf16_hkv3_s_straddle", 1, 300, 6, 3, 128, 100, 4, torch.bfloat16, 2.0),
+    ("bf16_hkv12_two_groups", 2, 333, 24, 12, 128, 192, 64, torch.bfloat16, 2.0),
+    ("bf16_hkv10_d64_two_groups", 1, 190, 10, 10, 64, 128, 32, torch.bfloat16, 2.0),
 ]
 
 

@@ -56,6 +56,7 @@ SE_SMALL = [
     ("bf16_L65_w64", 2, 65, 2, 2, 64, 4, 64, torch.bfloat16, 2.0),
     ("bf16_g7_w33_ragged", 3, 259, 2, 1, 128, 7, 33, torch.bfloat16, 2.0),
     ("bf16_hkv6_d64", 1, 300, 6, 6, 64, 4, 100, torch.bfloat16, 2.0),
+    ("bf16_hkv9_two_groups", 1, 270, 9, 9, 128, 4, 64, torch.bfloat16, 2.0),
 ]
 
 
