@@ -360,16 +360,17 @@ __global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
 //    row and 2 frequencies: it makes their cos/sin pairs once and turns those
 //    pairs in every head of the unit (4-byte loads and stores; 32 lanes cover
 //    a half row, one 128-byte run).
-//  * V unit: 64 keys x 64 dims of one head.  The wave writes the rows into
-//    its own LDS rows transposed (one LDS row per dim, keys in the order of
-//    vt_perm), then stores each dim's 64 keys as 16-byte runs of 8: whole
-//    128-byte lines of the V^T tile.
+//  * V unit: 64 keys x 64 dims of one head.  In two halves of 32 keys, the
+//    wave writes the rows into its own LDS rows transposed (one LDS row per
+//    dim, keys in the order of vt_perm), then stores each dim's keys as
+//    16-byte runs of 8; the two halves of every 128-byte V^T line come from
+//    the same wave moments apart.
 // The grid is twice the workgroups that fit on the chip at once; wave w takes
 // units w, w + W, w + 2W, ... (W waves in all).
 constexpr int kPrepKeyHeads = 8;
 constexpr int kPrepKeyWords = 1;   // 32-bit words (2 frequencies each) per lane and half row
 constexpr int kPrepVKeys = 64;     // keys per V unit
-constexpr int kPrepVRow = kPrepVKeys + 8;   // LDS row of a V unit (one dim), bf16
+constexpr int kPrepVRow = kPrepVKeys / 2 + 8;   // LDS row of one dim, half a V unit's keys, bf16
 
 // NW consecutive 32-bit words with the non-temporal hint / a plain store.
 template <int NW>
@@ -496,19 +497,18 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a, int64_t
         store_words<NW>(d + half, y2);
       }
     } else {
-      // ---- V unit u - kc: (sequence b, 64-key tile t, head h, dims dh * 64.., keys kh * 32..)
-      constexpr int NKH = kPrefillTileKeys / kPrepVKeys, VL = kPrepVKeys / 8;
+      // ---- V unit u - kc: (sequence b, 64-key tile t, head h, dims dh * 64 ..)
+      constexpr int VL = kPrepVKeys / 8;   // 16-byte loads per lane
       int64_t vv = u - kc;
-      const int kh = (int)(vv % NKH);
-      vv /= NKH;
       const int dh = (int)(vv % ND);
       vv /= ND;
       const int h = (int)(vv % a.Hkv);
       vv /= a.Hkv;
       const int t = (int)(vv % nT), b = (int)(vv / nT);
       const int Lb = a.per_seq ? a.seq_len[b] : a.L;
-      const int jb = t * kPrefillTileKeys + kh * kPrepVKeys;
-      // zero past the valid rows and for unreadable pages
+      const int jb = t * kPrefillTileKeys;
+      // zero past the valid rows and for unreadable pages; lane item it holds
+      // 8 dims of key row (lane >> 3) + 8 * it
       uint4 x[VL];
 #pragma unroll
       for (int it = 0; it < VL; ++it) {
@@ -524,25 +524,30 @@ __global__ void __launch_bounds__(256) kv_prep_bf16_kernel(KvPrepArgs a, int64_t
                          : make_uint4(0, 0, 0, 0);
         }
       }
+      // transposed in two halves of 32 keys through the wave's 32-key LDS rows
+      // (vt_perm keeps each 16-key group in place, so a half is self-contained)
       uint16_t(*vs)[kPrepVRow] = vsh[wave];
+      uint16_t* dst = (uint16_t*)a.vt + ((((int64_t)b * a.Hkv + h) * nT + t) * D + dh * 64) * kPrefillTileKeys;
 #pragma unroll
-      for (int it = 0; it < VL; ++it) {
-        const int i = lane + it * 64, row = i >> 3, dg = i & 7;
-        const int slot = vt_perm(row);
-        const uint32_t w4[4] = {x[it].x, x[it].y, x[it].z, x[it].w};
+      for (int hk = 0; hk < 2; ++hk) {
+        if (hk) wave_lds_sync();   // the first half's LDS reads come before these writes
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          vs[dg * 8 + 2 * q][slot] = (uint16_t)(w4[q] & 0xffffu);
-          vs[dg * 8 + 2 * q + 1][slot] = (uint16_t)(w4[q] >> 16);
+        for (int it = hk * VL / 2; it < (hk + 1) * VL / 2; ++it) {
+          const int i = lane + it * 64, row = (i >> 3) - hk * 32, dg = i & 7;
+          const int slot = vt_perm(row);
+          const uint32_t w4[4] = {x[it].x, x[it].y, x[it].z, x[it].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            vs[dg * 8 + 2 * q][slot] = (uint16_t)(w4[q] & 0xffffu);
+            vs[dg * 8 + 2 * q + 1][slot] = (uint16_t)(w4[q] >> 16);
+          }
         }
-      }
-      wave_lds_sync();
-      uint16_t* dst = (uint16_t*)a.vt + ((((int64_t)b * a.Hkv + h) * nT + t) * D + dh * 64) * kPrefillTileKeys +
-                      kh * kPrepVKeys;
+        wave_lds_sync();
 #pragma unroll
-      for (int it = 0; it < VL; ++it) {
-        const int i = lane + it * 64, dl = i / VL, kg = i % VL;
-        *(uint4*)(dst + dl * kPrefillTileKeys + kg * 8) = *(const uint4*)&vs[dl][kg * 8];
+        for (int it = 0; it < 4; ++it) {
+          const int i = lane + it * 64, dl = i >> 2, kg = i & 3;
+          *(uint4*)(dst + dl * kPrefillTileKeys + hk * 32 + kg * 8) = *(const uint4*)&vs[dl][kg * 8];
+        }
       }
       wave_lds_sync();   // this unit's LDS reads come before the next unit's writes
     }
@@ -591,7 +596,7 @@ template <int D, int PM, bool PAGED>
 static hipError_t launch_prep_bf16(const KvPrepArgs& a, hipStream_t st) {
   constexpr int half = D / 2, RK = 64 / (half / (2 * kPrepKeyWords)), ND = D / 64;
   const int64_t nK = (int64_t)a.B * (a.Lp / RK) * ((a.Hkv + kPrepKeyHeads - 1) / kPrepKeyHeads);
-  const int64_t nV = a.vt ? (int64_t)a.B * (a.Lp / kPrefillTileKeys) * a.Hkv * ND * (kPrefillTileKeys / kPrepVKeys) : 0;
+  const int64_t nV = a.vt ? (int64_t)a.B * (a.Lp / kPrefillTileKeys) * a.Hkv * ND : 0;
   int resident = 0;
   const hipError_t e = resident_workgroups(kv_prep_bf16_kernel<D, PM, PAGED>, &resident);
   if (e != hipSuccess) return e;
