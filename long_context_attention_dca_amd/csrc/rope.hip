@@ -354,7 +354,8 @@ __global__ void __launch_bounds__(256) kv_prep_f32_kernel(KvPrepArgs a) {
 // bf16 prepare pass.  Every wave works through its own share of a flat list of
 // units in which K and V units are interleaved in proportion, so that the
 // reads, the writes and the K rotation's fp64 arithmetic of different waves
-// overlap; no wave waits for another.
+// overlap; past the workgroup's start (where the first wave makes the
+// frequencies theta_k into LDS) no wave waits for another.
 //  * K unit: RK consecutive key rows (RK = 256 / D: 2 for D 128, 4 for
 //    D 64) of one sequence and up to kPrepKeyHeads KV heads.  A lane owns one
 //    row and 2 frequencies: it makes their cos/sin pairs once and turns those
